@@ -1,0 +1,17 @@
+"""QLoRA's frozen-base linear layer on AMD Instinct MI355X (gfx950).
+
+NF4 weights with double-quantized absmax constants, dequantized on the fly
+inside bf16 MFMA matmuls, plus a 16-bit LoRA branch, forward and backward.
+The computation lives in libqlora_mi355x.so (C ABI: include/qlora.h); this
+package only marshals torch tensors to it.
+"""
+
+from ._capi import EXPORTED, LIB_PATH, QLoRAError, lib, status_string  # noqa: F401
+from .ops import (NF4Weight, QLoRALinear, QLoRALinearFn, linear_bwd, linear_fwd, lora_down,  # noqa: F401
+                  lora_grad_in, lora_grads, nf4_matmul_dx, nf4_matmul_fwd, nf4_sizes)
+
+__all__ = [
+    "NF4Weight", "QLoRALinear", "QLoRALinearFn", "linear_fwd", "linear_bwd", "lora_down",
+    "nf4_matmul_fwd", "lora_grad_in", "nf4_matmul_dx", "lora_grads", "nf4_sizes", "lib",
+    "QLoRAError", "status_string",
+]

@@ -1,0 +1,94 @@
+"""ctypes declarations of libqlora_mi355x.so (the C ABI in include/qlora.h).
+
+Loading the library does not touch the GPU.  A missing library is an error:
+there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_mi355x.so")
+
+QLORA_OK = 0
+QLORA_ERR_INVALID_ARG = -1
+QLORA_ERR_UNSUPPORTED_SHAPE = -2
+QLORA_ERR_WORKSPACE = -3
+QLORA_ERR_HIP = -4
+
+EXPORTED = (
+    "qlora_status_string", "qlora_version", "qlora_nf4_sizes",
+    "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_dequantize_nf4",
+    "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in", "qlora_nf4_matmul_dx",
+    "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
+)
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, status_string(status), status))
+
+
+class NF4WeightStruct(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("code8", ctypes.c_void_p),
+        ("c2", ctypes.c_void_p),
+        ("mean", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+_vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_wp = ctypes.POINTER(NF4WeightStruct)
+
+_SIGS = {
+    "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_version": (ctypes.c_int, []),
+    "qlora_nf4_sizes": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "qlora_quantize_workspace_bytes": (_sz, [_i64]),
+    "qlora_quantize_nf4": (ctypes.c_int, [_vp, _wp, _vp, _sz, _vp]),
+    "qlora_dequantize_nf4": (ctypes.c_int, [_wp, _vp, _vp]),
+    "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, ctypes.c_int]),
+    "qlora_linear_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_bwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]),
+    "qlora_lora_down": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _vp, _vp]),
+    "qlora_nf4_matmul_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_lora_grad_in": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _vp, _vp]),
+    "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_lora_grads_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _sz,
+                                        _vp]),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libqlora_mi355x.so is not built (expected at %s); run "
+                "`python -m bit_nf4_quantized_absmax_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def check(status, where):
+    if status != QLORA_OK:
+        raise QLoRAError(status, where)

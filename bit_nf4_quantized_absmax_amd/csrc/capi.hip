@@ -1,0 +1,261 @@
+// C ABI of libqlora_mi355x: argument validation, workspace carving and the
+// composite forward / backward passes.  Every check runs before anything is
+// launched, so an error leaves all outputs untouched.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/qlora.h"
+#include "launch.h"
+
+using namespace qlora;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;  // kernels index rows * cols in int32 where safe
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_weight(const qlora_nf4_weight *w) {
+  if (!w) return QLORA_ERR_INVALID_ARG;
+  if (w->rows < 1 || w->cols < 1) return QLORA_ERR_INVALID_ARG;
+  if (w->rows > kMaxElems / w->cols) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!w->packed || !w->code8 || !w->c2 || !w->mean) return QLORA_ERR_INVALID_ARG;
+  if (!aligned(w->packed, 16) || !aligned(w->code8, 4) || !aligned(w->c2, 4) || !aligned(w->mean, 4))
+    return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+// Shape rules of the matmul entry points.
+int check_linear_shape(int64_t M, const qlora_nf4_weight *w, int32_t r, float scale) {
+  int st = check_weight(w);
+  if (st) return st;
+  if (M < 0 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
+  const int64_t N = w->rows, K = w->cols;
+  if (K % 64 != 0 || N % 8 != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M > 0 && (M > kMaxElems / std::max(N, K))) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  return QLORA_OK;
+}
+
+bool bf16_ok(const void *p) { return p && aligned(p, 16); }
+bool bf16_opt(const void *p) { return !p || aligned(p, 16); }
+
+NF4View view_of(const qlora_nf4_weight *w) {
+  return NF4View{w->packed, w->code8, w->c2, w->mean, static_cast<int>(w->rows), static_cast<int>(w->cols)};
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+size_t bf16_bytes(int64_t n) { return round_up(static_cast<size_t>(n) * 2, 256); }
+
+// Workspace of the forward pass: T [M, r] when the caller passes no T_out.
+size_t fwd_ws(int64_t M, int32_t r) { return bf16_bytes(M * r); }
+
+// Workspace of the backward pass: T (recompute) | G | dA partials | dB partials.
+struct BwdWs {
+  size_t t, g, pa, pb, total;
+};
+BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdWs w;
+  w.t = bf16_bytes(M * r);
+  w.g = bf16_bytes(M * r);
+  w.pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
+  w.pb = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r), 256);
+  w.total = w.t + w.g + w.pa + w.pb;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "QLORA_OK";
+    case QLORA_ERR_INVALID_ARG: return "QLORA_ERR_INVALID_ARG: null, misaligned or out-of-range argument";
+    case QLORA_ERR_UNSUPPORTED_SHAPE:
+      return "QLORA_ERR_UNSUPPORTED_SHAPE: need K % 64 == 0, N % 8 == 0, 1 <= r <= 128, sizes < 2^31";
+    case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
+    case QLORA_ERR_HIP: return "QLORA_ERR_HIP: HIP runtime or launch failure";
+    default: return "QLORA: unknown status";
+  }
+}
+
+int qlora_version(void) { return 10000; }
+
+int qlora_nf4_sizes(int64_t n, int64_t *packed_bytes, int64_t *nb, int64_t *nb2) {
+  if (n < 1) return QLORA_ERR_INVALID_ARG;
+  const int64_t b = (n + 63) / 64;
+  if (packed_bytes) *packed_bytes = (n + 1) / 2;
+  if (nb) *nb = b;
+  if (nb2) *nb2 = (b + 255) / 256;
+  return QLORA_OK;
+}
+
+size_t qlora_quantize_workspace_bytes(int64_t n) { return n < 1 ? 0 : quantize_ws_bytes(n); }
+
+int qlora_quantize_nf4(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_weight(out);
+  if (st) return st;
+  if (!W || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
+  const int64_t n = out->rows * out->cols;
+  if (!ws || !aligned(ws, 16) || ws_bytes < quantize_ws_bytes(n)) return QLORA_ERR_WORKSPACE;
+  return from_hip(launch_quantize(W, n, out->packed, out->code8, out->c2, out->mean, ws,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if (!bf16_ok(out_bf16)) return QLORA_ERR_INVALID_ARG;
+  return from_hip(launch_dequantize(w->packed, w->code8, w->c2, w->mean, w->rows * w->cols, out_bf16,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd) {
+  if (M < 0 || N < 1 || K < 64 || K % 64 || N % 8 || r < 1 || r > 128) return 0;
+  if (M > 0 && M > kMaxElems / std::max(N, K)) return 0;
+  return is_bwd ? bwd_ws(M, N, K, r).total : fwd_ws(M, r);
+}
+
+int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r, uint16_t *T,
+                    void *stream) {
+  if (M < 0 || K < 8 || K % 8 || r < 1 || r > 128) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M > kMaxElems / K) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(T)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_lora_down(X, static_cast<int>(M), static_cast<int>(K), A, r, T,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r, uint16_t *G,
+                       void *stream) {
+  if (M < 0 || N < 8 || N % 8 || r < 1 || r > 128) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M > kMaxElems / N) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!bf16_ok(dY) || !bf16_ok(B) || !bf16_ok(G)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_lora_grad_in(dY, static_cast<int>(M), static_cast<int>(N), B, r, G,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int qlora_nf4_matmul_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *T,
+                         const uint16_t *B, int32_t r, float scale, uint16_t *Y, void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!bf16_ok(X) || !bf16_ok(T) || !bf16_ok(B) || !bf16_ok(Y)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_matmul_fwd(X, static_cast<int>(M), view_of(W), T, B, r, scale, Y,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W, const uint16_t *G,
+                        const uint16_t *A, int32_t r, float scale, uint16_t *dX, void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!bf16_ok(dY) || !bf16_ok(G) || !bf16_ok(A) || !bf16_ok(dX)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_matmul_dx(dY, static_cast<int>(M), view_of(W), G, A, r, scale, dX,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M < 0 || N < 1 || K < 1 || r < 1 || r > 128) return 0;
+  return round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256) +
+         round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r), 256);
+}
+
+int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, const uint16_t *T, int64_t M,
+                     int64_t N, int64_t K, int32_t r, float scale, uint16_t *dA, uint16_t *dB, void *ws,
+                     size_t ws_bytes, void *stream) {
+  if (M < 0 || N < 1 || K < 1 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
+  if (r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M > 0 && M > kMaxElems / std::max(N, K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
+  if (dA && (!bf16_ok(X) || !bf16_ok(G))) return QLORA_ERR_INVALID_ARG;
+  if (dB && (!bf16_ok(dY) || !bf16_ok(T))) return QLORA_ERR_INVALID_ARG;
+  const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
+  if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grads_workspace_bytes(M, N, K, r))
+    return QLORA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int m = static_cast<int>(M);
+  if (dA) {
+    hipError_t e = launch_lora_grad_w(X, G, m, static_cast<int>(K), r, scale, true, dA, ws, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dB) {
+    hipError_t e = launch_lora_grad_w(dY, T, m, static_cast<int>(N), r, scale, false, dB,
+                                      static_cast<char *>(ws) + pa, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *A,
+                     const uint16_t *B, int32_t r, float scale, uint16_t *Y, uint16_t *T_out, void *ws,
+                     size_t ws_bytes, void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B) || !bf16_ok(Y) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
+  uint16_t *T = T_out;
+  if (!T) {
+    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, r)) return QLORA_ERR_WORKSPACE;
+    T = static_cast<uint16_t *>(ws);
+  }
+  if (M == 0) return QLORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const NF4View v = view_of(W);
+  const int m = static_cast<int>(M);
+  hipError_t e = launch_lora_down(X, m, v.K, A, r, T, s);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  return from_hip(launch_matmul_fwd(X, m, v, T, B, r, scale, Y, s));
+}
+
+int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,
+                     const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
+                     uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!bf16_ok(dY) || !bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B)) return QLORA_ERR_INVALID_ARG;
+  if (!bf16_opt(T) || !bf16_opt(dX) || !bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
+  const BwdWs L = bwd_ws(M, W->rows, W->cols, r);
+  if (!ws || !aligned(ws, 16) || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const NF4View v = view_of(W);
+  const int m = static_cast<int>(M);
+  char *base = static_cast<char *>(ws);
+  uint16_t *Tw = reinterpret_cast<uint16_t *>(base);
+  uint16_t *G = reinterpret_cast<uint16_t *>(base + L.t);
+  void *pa = base + L.t + L.g;
+  void *pb = base + L.t + L.g + L.pa;
+  hipError_t e = hipSuccess;
+  if (dX || dA) {
+    e = launch_lora_grad_in(dY, m, v.N, B, r, G, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dX) {
+    e = launch_matmul_dx(dY, m, v, G, A, r, scale, dX, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dA) {
+    e = launch_lora_grad_w(X, G, m, v.K, r, scale, true, dA, pa, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dB) {
+    const uint16_t *Tu = T;
+    if (!Tu) {
+      e = launch_lora_down(X, m, v.K, A, r, Tw, s);
+      if (e != hipSuccess) return QLORA_ERR_HIP;
+      Tu = Tw;
+    }
+    e = launch_lora_grad_w(dY, Tu, m, v.N, r, scale, false, dB, pb, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

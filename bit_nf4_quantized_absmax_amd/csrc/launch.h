@@ -1,0 +1,54 @@
+// Host-side launchers of the gfx950 kernels (internal to libqlora_mi355x).
+// Arguments are validated by the C ABI layer before any of these is called;
+// each returns the hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+// ---- codec ---------------------------------------------------------------
+// Workspace layout for quantize: absmax fp32 [nb] | tree partials fp64.
+size_t quantize_ws_bytes(int64_t n);
+hipError_t launch_quantize(const float *W, int64_t n, uint8_t *packed, uint8_t *code8, float *c2,
+                           float *mean, void *ws, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
+                             const float *mean, int64_t n, uint16_t *out, hipStream_t s);
+
+// ---- NF4 weight view passed to the matmul kernels ---------------------------
+struct NF4View {
+  const uint8_t *packed;
+  const uint8_t *code8;
+  const float *c2;
+  const float *mean;
+  int N;  // rows (output features)
+  int K;  // columns (input features), multiple of 64
+};
+
+// ---- large-M matmuls -----------------------------------------------------------
+hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
+                             const uint16_t *B, int r, float scale, uint16_t *Y, hipStream_t s);
+hipError_t launch_matmul_dx(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
+                            const uint16_t *A, int r, float scale, uint16_t *dX, hipStream_t s);
+
+// ---- LoRA skinny products ------------------------------------------------------
+// T [M, r] = X [M, K] A^T  (A [r, K])
+hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, uint16_t *T,
+                            hipStream_t s);
+// G [M, r] = dY [M, N] B  (B [N, r])
+hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r,
+                               uint16_t *G, hipStream_t s);
+// out = scale * P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB).
+size_t lora_grad_ws_bytes(int M, int D, int r);
+hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, float scale,
+                              bool out_r_major, uint16_t *out, void *ws, hipStream_t s);
+
+// ---- small-M forward ------------------------------------------------------------
+int small_m_max();
+hipError_t launch_small_m_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *A,
+                              const uint16_t *B, int r, float scale, uint16_t *Y, uint16_t *T,
+                              hipStream_t s);
+
+}  // namespace qlora

@@ -1,0 +1,261 @@
+// NF4 + double-quantization codec kernels for gfx950.
+//
+// Quantize (automatone.win, "QLoRA paper explained", How it works / 4-bit
+// NormalFloat and Double Quantization; creativeworksofknowledge.com, "QLoRA:
+// Fine-Tune 70B on One GPU", The three innovations / 1-2):
+//   pass 1  k_quant_blocks   one read of W: per-64 absmax, NF4 codes, nibbles
+//   pass 2  k_tree_sum       fp64 pairwise tree of the absmax values (fixed
+//                            order, one or more levels of aligned 2048-chunks)
+//   pass 3  k_quant_consts   mean, per-256 scale c2, 8-bit constant codes
+// Dequantize: k_dequant     packed codes -> bf16, one read, one write.
+//
+// Bit-exactness rules: fp32 division is IEEE correctly rounded (hipcc's
+// default), no fused multiply-add (-ffp-contract=off), bf16 conversion is
+// round-to-nearest-even, the tree order is fixed.
+#include "common.h"
+#include "launch.h"
+
+namespace qlora {
+
+__constant__ uint32_t cNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
+__constant__ uint32_t cNF4Thresh[15] = {QLORA_NF4_THRESH_BITS};
+__constant__ uint32_t cT8Level[256] = {QLORA_T8_LEVEL_BITS};
+__constant__ uint32_t cT8Thresh[255] = {QLORA_T8_THRESH_BITS};
+
+constexpr int kTreeChunk = 2048;   // elements reduced by one workgroup of k_tree_sum
+constexpr int kThreads = 256;
+
+// Nearest NF4 level, ties to the lower code: number of thresholds below x.
+__device__ __forceinline__ uint32_t nf4_code(float x) {
+  uint32_t q = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) q += (x > u2f(cNF4Thresh[i])) ? 1u : 0u;
+  return q;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1.  Each lane owns 4 consecutive elements; 16 lanes form one block of
+// 64.  The lane group reduces |w| with cross-lane max, every lane divides its
+// elements by the block absmax and codes them, and writes its 2 packed bytes.
+// Elements past n do not exist: they do not enter the max and pack as 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_quant_blocks(const float *__restrict__ W, int64_t n,
+                                                           uint8_t *__restrict__ packed,
+                                                           float *__restrict__ absmax) {
+  const int64_t nchunks = ((n + kBlock - 1) / kBlock) * 16;  // 4-element chunks, whole blocks
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nchunks; c += stride) {
+    const int64_t e = c * 4;
+    float w[4];
+    const bool full = (e + 3 < n);
+    if (full) {
+      const float4 v = *reinterpret_cast<const float4 *>(W + e);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (e + i < n) ? W[e + i] : 0.0f;
+    }
+    float a = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
+
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[i] = (a > 0.0f) ? nf4_code(w[i] / a) : 7u;
+      if (e + i >= n) q[i] = 0u;
+    }
+    const uint32_t b0 = q[0] | (q[1] << 4), b1 = q[2] | (q[3] << 4);
+    uint8_t *dst = packed + (e >> 1);
+    if (full) {
+      *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(b0 | (b1 << 8));
+    } else {
+      if (e < n) dst[0] = static_cast<uint8_t>(b0);
+      if (e + 2 < n) dst[1] = static_cast<uint8_t>(b1);
+    }
+    if ((threadIdx.x & 15) == 0) absmax[c >> 4] = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2.  Workgroup g reduces in[2048 g, 2048 g + 2048) (zero beyond len) to
+// one fp64 value with the neighbour-pairing tree: 8 values per thread
+// ((v0+v1)+(v2+v3))+((v4+v5)+(v6+v7)), then level by level in LDS,
+// s'[t] = s[2t] + s[2t+1].  Because chunks are aligned powers of two,
+// applying this again to the partials reproduces the global tree exactly.
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ in, int64_t len,
+                                                       double *__restrict__ out) {
+  __shared__ double s[kThreads];
+  const int t = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kTreeChunk + t * 8;
+  double v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (base + i < len) ? static_cast<double>(in[base + i]) : 0.0;
+  s[t] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  __syncthreads();
+  for (int width = kThreads / 2; width >= 1; width >>= 1) {
+    double tmp = 0.0;
+    if (t < width) tmp = s[2 * t] + s[2 * t + 1];
+    __syncthreads();
+    if (t < width) s[t] = tmp;
+    __syncthreads();
+  }
+  if (t == 0) out[blockIdx.x] = s[0];
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3.  mean = fl32(sum / nb).  One wave per group of 256 constants, 4 per
+// lane: d = fl32(c - mean), c2 = max |d| over the group, code = number of T8
+// thresholds below fl32(d / c2) (binary search over the 255 thresholds, with
+// +inf as a 256th sentinel).  c2 = 0 -> code 127.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restrict__ absmax, int64_t nb,
+                                                           const double *__restrict__ sum,
+                                                           uint8_t *__restrict__ code8,
+                                                           float *__restrict__ c2,
+                                                           float *__restrict__ mean_out) {
+  __shared__ float thr[256];
+  for (int i = threadIdx.x; i < 256; i += kThreads) thr[i] = (i < 255) ? u2f(cT8Thresh[i]) : INFINITY;
+  __syncthreads();
+  const float mean = static_cast<float>(sum[0] / static_cast<double>(nb));
+  if (blockIdx.x == 0 && threadIdx.x == 0) mean_out[0] = mean;
+
+  const int lane = threadIdx.x & 63;
+  const int64_t nb2 = (nb + kGroup - 1) / kGroup;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6); g < nb2;
+       g += waves) {
+    const int64_t idx = g * kGroup + lane * 4;
+    float d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = (idx + i < nb) ? (absmax[idx + i] - mean) : 0.0f;
+    float m = fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3])));
+    m = wave_max(m);
+    uint32_t codes = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = 127;
+      if (m > 0.0f) {
+        const float x = d[i] / m;
+        lo = 0;
+#pragma unroll
+        for (int step = 128; step >= 1; step >>= 1)
+          if (thr[lo + step - 1] < x) lo += step;
+      }
+      codes |= lo << (8 * i);
+    }
+    if (idx + 3 < nb) {
+      *reinterpret_cast<uint32_t *>(code8 + idx) = codes;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (idx + i < nb) code8[idx + i] = static_cast<uint8_t>(codes >> (8 * i));
+    }
+    if (lane == 0) c2[g] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: each thread expands 8 consecutive elements (4 packed bytes) into
+// one 16-byte store of bf16.  All 8 share one block constant (8 | 64).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict__ packed,
+                                                      const uint8_t *__restrict__ code8,
+                                                      const float *__restrict__ c2,
+                                                      const float *__restrict__ mean_p, int64_t n,
+                                                      uint16_t *__restrict__ out) {
+  __shared__ float lut[16];
+  __shared__ float t8[256];
+  if (threadIdx.x < 16) lut[threadIdx.x] = u2f(cNF4Level[threadIdx.x]);
+  for (int i = threadIdx.x; i < 256; i += kThreads) t8[i] = u2f(cT8Level[i]);
+  __syncthreads();
+  const float mean = mean_p[0];
+  const int64_t nchunks = (n + 7) / 8;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nchunks; c += stride) {
+    const int64_t e = c * 8;
+    const int64_t b = e >> 6;
+    const float chat = decode_absmax(t8[code8[b]], c2[b >> 8], mean);
+    const bool full = (e + 7 < n);
+    uint32_t p;
+    if (full) {
+      p = *reinterpret_cast<const uint32_t *>(packed + (e >> 1));
+    } else {
+      p = 0;
+      for (int i = 0; i < 4; ++i)
+        if (e + 2 * i < n) p |= static_cast<uint32_t>(packed[(e >> 1) + i]) << (8 * i);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = lut[(p >> (8 * i)) & 15u] * chat;
+      const float hi = lut[(p >> (8 * i + 4)) & 15u] * chat;
+      o[i] = pack_bf16x2(lo, hi);
+    }
+    if (full) {
+      *reinterpret_cast<uint4 *>(out + e) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      for (int i = 0; i < 8; ++i)
+        if (e + i < n) out[e + i] = static_cast<uint16_t>(o[i >> 1] >> (16 * (i & 1)));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static int64_t tree_partials(int64_t len) { return (len + kTreeChunk - 1) / kTreeChunk; }
+
+static unsigned grid_for(int64_t work_items, int64_t per_wg, int64_t cap) {
+  int64_t g = (work_items + per_wg - 1) / per_wg;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return static_cast<unsigned>(g);
+}
+
+size_t quantize_ws_bytes(int64_t n) {
+  if (n < 1) return 0;
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t p1 = tree_partials(nb);
+  // absmax fp32 [nb] (padded to 256 B) | two ping-pong fp64 partial buffers [p1]
+  const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
+  return a + 2 * static_cast<size_t>(p1) * 8;
+}
+
+hipError_t launch_quantize(const float *W, int64_t n, uint8_t *packed, uint8_t *code8, float *c2,
+                           float *mean, void *ws, hipStream_t s) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
+  float *absmax = static_cast<float *>(ws);
+  double *buf0 = reinterpret_cast<double *>(static_cast<char *>(ws) + a);
+  double *buf1 = buf0 + tree_partials(nb);
+
+  hipLaunchKernelGGL(k_quant_blocks, dim3(grid_for(nb * 16, kThreads, 16384)), dim3(kThreads), 0, s, W,
+                     n, packed, absmax);
+  int64_t len = nb;
+  hipLaunchKernelGGL(k_tree_sum<float>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads), 0,
+                     s, absmax, len, buf0);
+  len = tree_partials(len);
+  double *cur = buf0, *nxt = buf1;
+  while (len > 1) {
+    hipLaunchKernelGGL(k_tree_sum<double>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads),
+                       0, s, cur, len, nxt);
+    len = tree_partials(len);
+    double *t = cur; cur = nxt; nxt = t;
+  }
+  const int64_t nb2 = (nb + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(k_quant_consts, dim3(grid_for(nb2, kThreads / 64, 4096)), dim3(kThreads), 0, s,
+                     absmax, nb, cur, code8, c2, mean);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
+                             const float *mean, int64_t n, uint16_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(k_dequant, dim3(grid_for((n + 7) / 8, kThreads, 16384)), dim3(kThreads), 0, s, packed,
+                     code8, c2, mean, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

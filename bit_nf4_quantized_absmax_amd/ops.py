@@ -1,0 +1,255 @@
+"""PyTorch-facing binding of libqlora_mi355x (argument marshalling only).
+
+Torch provides device memory and streams; every step of the computation runs
+in the HIP kernels behind the C ABI.  Tensors must be CUDA (HIP) tensors,
+contiguous, with the dtypes named below; work is enqueued on the current
+stream of the tensor's device.
+
+Layer (automatone.win, "QLoRA paper explained", How it works; aiwiki.com.my,
+"QLoRA", Key Concepts and Technology): frozen NF4 weight W [N, K] with double
+-quantized constants, bf16 compute, LoRA pair A [r, K], B [N, r], scale
+s = alpha / r:  Y = X deq(W)^T + s (X A^T) B^T.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._capi import NF4WeightStruct, check, lib
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def nf4_sizes(n):
+    pb, nb, nb2 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    check(lib().qlora_nf4_sizes(int(n), ctypes.byref(pb), ctypes.byref(nb), ctypes.byref(nb2)), "qlora_nf4_sizes")
+    return pb.value, nb.value, nb2.value
+
+
+@dataclass
+class NF4Weight:
+    """A frozen weight [rows, cols] in NF4 with double-quantized constants.
+
+    packed uint8 [ceil(n/2)], code8 uint8 [nb], c2 float32 [nb2], mean float32 [1].
+    """
+    packed: torch.Tensor
+    code8: torch.Tensor
+    c2: torch.Tensor
+    mean: torch.Tensor
+    rows: int
+    cols: int
+
+    @property
+    def shape(self):
+        return (self.rows, self.cols)
+
+    @property
+    def device(self):
+        return self.packed.device
+
+    def struct(self):
+        return NF4WeightStruct(self.packed.data_ptr(), self.code8.data_ptr(), self.c2.data_ptr(),
+                               self.mean.data_ptr(), self.rows, self.cols)
+
+    @classmethod
+    def empty(cls, rows, cols, device):
+        pb, nb, nb2 = nf4_sizes(rows * cols)
+        return cls(torch.empty(pb, dtype=torch.uint8, device=device),
+                   torch.empty(nb, dtype=torch.uint8, device=device),
+                   torch.empty(nb2, dtype=torch.float32, device=device),
+                   torch.empty(1, dtype=torch.float32, device=device), rows, cols)
+
+    @classmethod
+    def quantize(cls, W):
+        """Quantize a float32 [rows, cols] device tensor (qlora_quantize_nf4)."""
+        if W.dim() != 2:
+            raise ValueError("W must be 2-D [out_features, in_features]")
+        _need(W, torch.float32, "W")
+        rows, cols = W.shape
+        w = cls.empty(rows, cols, W.device)
+        ws_bytes = lib().qlora_quantize_workspace_bytes(rows * cols)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=W.device)
+        st = w.struct()
+        check(lib().qlora_quantize_nf4(_ptr(W), ctypes.byref(st), _ptr(ws), ws_bytes, _stream(W)),
+              "qlora_quantize_nf4")
+        return w
+
+    def dequantize(self):
+        """bf16 [rows, cols] copy of the weight (qlora_dequantize_nf4)."""
+        out = torch.empty(self.rows, self.cols, dtype=torch.bfloat16, device=self.device)
+        st = self.struct()
+        check(lib().qlora_dequantize_nf4(ctypes.byref(st), _ptr(out), _stream(out)), "qlora_dequantize_nf4")
+        return out
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.packed, self.code8, self.c2, self.mean))
+
+
+def _lin_checks(X, w, A, B, r_expect=None):
+    N, K = w.rows, w.cols
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [M, %d]" % K)
+    _need(X, torch.bfloat16, "X")
+    r = A.shape[0]
+    _need(A, torch.bfloat16, "A", (r, K))
+    _need(B, torch.bfloat16, "B", (N, r))
+    return X.shape[0], N, K, r
+
+
+def linear_fwd(X, w, A, B, scale, T_out=None):
+    """Y = X deq(W)^T + scale (X A^T) B^T; returns (Y, T) with T = X A^T [M, r]."""
+    M, N, K, r = _lin_checks(X, w, A, B)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    _need(T, torch.bfloat16, "T", (M, r))
+    st = w.struct()
+    check(lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(Y),
+                                 _ptr(T), None, 0, _stream(X)), "qlora_linear_fwd")
+    return Y, T
+
+
+def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=True, workspace=None):
+    """Returns (dX, dA, dB) (None where not requested); T may be None (recomputed)."""
+    M, N, K, r = _lin_checks(X, w, A, B)
+    _need(dY, torch.bfloat16, "dY", (M, N))
+    if T is not None:
+        _need(T, torch.bfloat16, "T", (M, r))
+    dev = X.device
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev) if need_dX else None
+    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev) if need_dA else None
+    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
+    ws_bytes = lib().qlora_linear_workspace_bytes(M, N, K, r, 1)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    st = w.struct()
+    check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(T), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
+                                 float(scale), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(X)),
+          "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+# ---- the individual steps ------------------------------------------------------
+
+def lora_down(X, A, out=None):
+    M, K = X.shape
+    r = A.shape[0]
+    _need(X, torch.bfloat16, "X")
+    _need(A, torch.bfloat16, "A", (r, K))
+    T = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    check(lib().qlora_lora_down(_ptr(X), M, K, _ptr(A), r, _ptr(T), _stream(X)), "qlora_lora_down")
+    return T
+
+
+def nf4_matmul_fwd(X, w, T, B, scale, out=None):
+    M = X.shape[0]
+    r = B.shape[1]
+    _need(X, torch.bfloat16, "X", (M, w.cols))
+    _need(T, torch.bfloat16, "T", (M, r))
+    _need(B, torch.bfloat16, "B", (w.rows, r))
+    Y = out if out is not None else torch.empty(M, w.rows, dtype=torch.bfloat16, device=X.device)
+    st = w.struct()
+    check(lib().qlora_nf4_matmul_fwd(_ptr(X), M, ctypes.byref(st), _ptr(T), _ptr(B), r, float(scale), _ptr(Y),
+                                     _stream(X)), "qlora_nf4_matmul_fwd")
+    return Y
+
+
+def lora_grad_in(dY, B, out=None):
+    M, N = dY.shape
+    r = B.shape[1]
+    _need(dY, torch.bfloat16, "dY")
+    _need(B, torch.bfloat16, "B", (N, r))
+    G = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=dY.device)
+    check(lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(B), r, _ptr(G), _stream(dY)), "qlora_lora_grad_in")
+    return G
+
+
+def nf4_matmul_dx(dY, w, G, A, scale, out=None):
+    M = dY.shape[0]
+    r = A.shape[0]
+    _need(dY, torch.bfloat16, "dY", (M, w.rows))
+    _need(G, torch.bfloat16, "G", (M, r))
+    _need(A, torch.bfloat16, "A", (r, w.cols))
+    dX = out if out is not None else torch.empty(M, w.cols, dtype=torch.bfloat16, device=dY.device)
+    st = w.struct()
+    check(lib().qlora_nf4_matmul_dx(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, float(scale), _ptr(dX),
+                                    _stream(dY)), "qlora_nf4_matmul_dx")
+    return dX
+
+
+def lora_grads(X, dY, G, T, scale, need_dA=True, need_dB=True, workspace=None):
+    M, K = X.shape
+    N = dY.shape[1]
+    r = G.shape[1]
+    dev = X.device
+    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev) if need_dA else None
+    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
+    ws_bytes = lib().qlora_lora_grads_workspace_bytes(M, N, K, r)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(G), _ptr(T), M, N, K, r, float(scale), _ptr(dA),
+                                 _ptr(dB), _ptr(ws), ws_bytes, _stream(X)), "qlora_lora_grads")
+    return dA, dB
+
+
+# ---- autograd ----------------------------------------------------------------
+
+class QLoRALinearFn(torch.autograd.Function):
+    """Y = X deq(W)^T + scale (X A^T) B^T with gradients for X, A and B only."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, w, scale):
+        Y, T = linear_fwd(X, w, A, B, scale)
+        ctx.save_for_backward(X, A, B, T)
+        ctx.w, ctx.scale = w, scale
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, A, B, T = ctx.saved_tensors
+        dX, dA, dB = linear_bwd(dY.contiguous(), X, T, ctx.w, A, B, ctx.scale,
+                                need_dX=ctx.needs_input_grad[0], need_dA=ctx.needs_input_grad[1],
+                                need_dB=ctx.needs_input_grad[2])
+        return dX, dA, dB, None, None
+
+
+class QLoRALinear(torch.nn.Module):
+    """A linear layer with a frozen NF4 base weight and a trainable LoRA pair.
+
+    No bias and no dropout (the adapter configuration uses bias="none").
+    """
+
+    def __init__(self, weight_fp32, r, alpha, lora_A=None, lora_B=None):
+        super().__init__()
+        self.w = NF4Weight.quantize(weight_fp32.contiguous())
+        N, K = self.w.shape
+        dev = weight_fp32.device
+        self.r = int(r)
+        self.scale = float(torch.tensor(alpha, dtype=torch.float32) / torch.tensor(r, dtype=torch.float32))
+        self.lora_A = torch.nn.Parameter(lora_A if lora_A is not None else
+                                         torch.zeros(r, K, dtype=torch.bfloat16, device=dev))
+        self.lora_B = torch.nn.Parameter(lora_B if lora_B is not None else
+                                         torch.zeros(N, r, dtype=torch.bfloat16, device=dev))
+
+    def forward(self, x):
+        lead = x.shape[:-1]
+        y = QLoRALinearFn.apply(x.reshape(-1, x.shape[-1]).contiguous(), self.lora_A, self.lora_B, self.w,
+                                self.scale)
+        return y.reshape(*lead, y.shape[-1])

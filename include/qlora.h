@@ -1,0 +1,175 @@
+/*
+ * qlora.h -- C ABI of libqlora_mi355x.so, the frozen-base QLoRA linear layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (automatone.win, "QLoRA paper explained", TL;DR and How it works;
+ * aiwiki.com.my, "QLoRA", Key Concepts and Technology): the frozen base
+ * weight W [N, K] is stored as 4-bit NormalFloat codes with one absmax
+ * constant per block of 64 weights; the constants are themselves quantized
+ * to 8-bit codes in groups of 256 around a per-tensor mean ("double
+ * quantization", creativeworksofknowledge.com, "QLoRA: Fine-Tune 70B on One
+ * GPU", The three innovations / 2).  Each pass dequantizes W to bf16 on the
+ * fly inside the matmul and adds a 16-bit LoRA branch:
+ *
+ *     T  = X A^T                    Y  = X deq(W)^T + s T B^T
+ *     G  = dY B                     dX = dY deq(W) + s G A
+ *     dA = s G^T X                  dB = s dY^T T
+ *
+ * with s = alpha / r.  No gradient is formed for W, which is frozen.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory and keeps no per-call state.  Scratch space
+ *    is passed in as a workspace (size from the *_workspace_bytes queries).
+ *  - bf16 tensors are passed as uint16_t bit patterns.  All tensors are
+ *    row-major and contiguous; every pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; the call returns without synchronizing.
+ *  - The status is returned synchronously.  Arguments are validated before
+ *    anything is launched: on any error nothing is launched or written.  A
+ *    failed launch returns QLORA_ERR_HIP.
+ *  - Gradients overwrite their outputs (no accumulation).
+ *  - Results are deterministic: no floating-point atomics are used, so two
+ *    calls on the same inputs give the same bits.
+ *  - Inputs with NaN or Inf are outside the contract (outputs unspecified).
+ */
+#ifndef QLORA_MI355X_H
+#define QLORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1,       /* null/misaligned pointer, negative size, bad scale */
+  QLORA_ERR_UNSUPPORTED_SHAPE = -2, /* K % 64 != 0, r outside [1, 128], size overflow */
+  QLORA_ERR_WORKSPACE = -3,         /* workspace missing or smaller than required */
+  QLORA_ERR_HIP = -4                /* a HIP runtime call or kernel launch failed */
+} qlora_status;
+
+/* One quantized weight W [rows = N, cols = K], n = rows * cols elements,
+ * flattened row-major.  Block b covers elements [64 b, 64 b + 64); group g
+ * covers blocks [256 g, 256 g + 256); the last block and group may be partial.
+ *   packed  [ceil(n/2)]   NF4 codes: byte j holds element 2j in its low
+ *                         nibble and element 2j+1 in its high nibble; for odd
+ *                         n the last high nibble is 0.
+ *   code8   [nb]          8-bit code of block b's absmax, an index into the
+ *                         ascending 256-entry constant table.
+ *   c2      [nb2]         fp32 scale of group g (max |absmax - mean|).
+ *   mean    [1]           fp32 mean of all block absmax values.
+ * with nb = ceil(n/64) and nb2 = ceil(nb/256).  The library reads and writes
+ * through these pointers; it does not own them. */
+typedef struct {
+  uint8_t *packed;
+  uint8_t *code8;
+  float *c2;
+  float *mean;
+  int64_t rows;
+  int64_t cols;
+} qlora_nf4_weight;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qlora_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int qlora_version(void);
+
+/* Storage sizes for n >= 1 elements: packed bytes, blocks (nb), groups (nb2).
+ * Any output pointer may be NULL.  Host-only; never touches the GPU. */
+int qlora_nf4_sizes(int64_t n, int64_t *packed_bytes, int64_t *nb, int64_t *nb2);
+
+/* Workspace bytes needed by qlora_quantize_nf4 for n elements (0 if n < 1). */
+size_t qlora_quantize_workspace_bytes(int64_t n);
+
+/* Quantize fp32 W [out->rows, out->cols] into *out (storage as above).
+ * Codes: x = fl32(w / absmax) (IEEE division), NF4 code = nearest of the 16
+ * levels with ties to the lower index (absmax 0 -> code 7); the block
+ * constants are centred on their mean (fp64 pairwise-tree sum in a fixed
+ * order, divided by nb, rounded to fp32) and coded to the nearest entry of
+ * the 8-bit table, ties low (group scale 0 -> code 127).  Bit-exact and
+ * deterministic.  Pages: automatone.win, "QLoRA paper explained", How it
+ * works / 4-bit NormalFloat and Double Quantization.
+ * Requires rows, cols >= 1 and ws_bytes >= qlora_quantize_workspace_bytes. */
+int qlora_quantize_nf4(const float *W, const qlora_nf4_weight *out, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* Dequantize *w to bf16 out [rows, cols]:
+ *   c_hat = fl32(fl32(T8[code8] * c2) + mean)      (no fused multiply-add)
+ *   out   = bf16_rne(fl32(NF4[q] * c_hat))
+ * Pages: automatone.win, "QLoRA paper explained", How it works (dequantize
+ * to BFloat16 on the fly). */
+int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *stream);
+
+/* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
+ * (is_bwd = 1) at these sizes.  0 if the shape is unsupported. */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd);
+
+/* Forward: Y [M, N] = X [M, K] deq(W)^T + scale (X A^T) B^T.
+ *   X [M, K], A [r, K], B [N, r], Y [M, N]: bf16.  W: N x K NF4 weight.
+ *   T_out [M, r] (nullable): receives T = X A^T in bf16 for reuse in the
+ *   backward pass; when NULL, T lives in the workspace.
+ * Requires K % 64 == 0 (blocks never straddle rows), 1 <= r <= 128, M >= 0
+ * (M = 0 launches nothing), N >= 1.  Pages: automatone.win, "QLoRA paper
+ * explained", How it works; creativeworksofknowledge.com, "QLoRA: Fine-Tune
+ * 70B on One GPU", Code (r, lora_alpha, bias="none"). */
+int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
+                     const uint16_t *A, const uint16_t *B, int32_t r, float scale,
+                     uint16_t *Y, uint16_t *T_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward: given dY [M, N], X [M, K] and optionally T = X A^T [M, r]
+ * (NULL: recomputed), writes
+ *   dX [M, K] = dY deq(W) + scale (dY B) A        (nullable: skipped)
+ *   dA [r, K] = scale (dY B)^T X                  (nullable: skipped)
+ *   dB [N, r] = scale dY^T T                      (nullable: skipped)
+ * all bf16.  No gradient for W (frozen).  Same shape rules as the forward.
+ * dA and dB are reduced over M in a fixed order (deterministic).
+ * Pages: automatone.win, "QLoRA paper explained", How it works (gradients
+ * flow through the 4-bit base into the adapters only); gptget.net, "QLoRA:
+ * Efficient Finetuning of Quantized LLMs", Deep Analysis / Methodology. */
+int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,
+                     const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B,
+                     int32_t r, float scale, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* ---- The individual steps of the two passes (same conventions) ---------- */
+
+/* T [M, r] = X [M, K] A^T, A [r, K]; bf16 in, bf16 out (fp32 accumulation). */
+int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r,
+                    uint16_t *T, void *stream);
+
+/* Y [M, N] = X deq(W)^T + scale T B^T, with T [M, r] given (the fused
+ * dequant-matmul with the LoRA up-projection folded in as one extra
+ * contraction step).  No workspace. */
+int qlora_nf4_matmul_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
+                         const uint16_t *T, const uint16_t *B, int32_t r, float scale,
+                         uint16_t *Y, void *stream);
+
+/* G [M, r] = dY [M, N] B, B [N, r]. */
+int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r,
+                       uint16_t *G, void *stream);
+
+/* dX [M, K] = dY deq(W) + scale G A, G [M, r] given.  No workspace. */
+int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W,
+                        const uint16_t *G, const uint16_t *A, int32_t r, float scale,
+                        uint16_t *dX, void *stream);
+
+/* Workspace bytes for qlora_lora_grads. */
+size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* dA [r, K] = scale G^T X and/or dB [N, r] = scale dY^T T (either output
+ * may be NULL), reduced over M in fp32 split-M partials plus a fixed-order
+ * second pass.  G/X are needed for dA, dY/T for dB. */
+int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
+                     const uint16_t *T, int64_t M, int64_t N, int64_t K, int32_t r,
+                     float scale, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_MI355X_H */

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/qlora.h declares, answers size queries, and rejects bad arguments
+before launching anything (these calls never reach the GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_nf4_quantized_absmax_amd as q
+from bit_nf4_quantized_absmax_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+OK, INVALID, SHAPE, WS = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = q.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(names) == sorted(_capi.EXPORTED)
+
+
+def test_status_strings_and_version():
+    for s in (OK, INVALID, SHAPE, WS, -4, 123):
+        assert isinstance(q.status_string(s), str) and q.status_string(s)
+    assert q.lib().qlora_version() == 10000
+
+
+def test_sizes():
+    assert q.nf4_sizes(1) == (1, 1, 1)
+    assert q.nf4_sizes(4096 * 4096) == (4096 * 4096 // 2, 262144, 1024)
+    assert q.nf4_sizes(11008 * 4096) == (11008 * 2048, 704512, 2752)
+    with pytest.raises(q.QLoRAError):
+        q.nf4_sizes(0)
+    L = q.lib()
+    assert L.qlora_quantize_workspace_bytes(0) == 0
+    assert L.qlora_quantize_workspace_bytes(64) >= 4
+    assert L.qlora_linear_workspace_bytes(8192, 4096, 4096, 64, 0) >= 8192 * 64 * 2
+    assert L.qlora_linear_workspace_bytes(8192, 4096, 4096, 64, 1) >= 2 * 8192 * 64 * 2
+    assert L.qlora_linear_workspace_bytes(8, 4096, 4000, 64, 0) == 0      # K % 64
+    assert L.qlora_linear_workspace_bytes(8, 4099, 4096, 64, 0) == 0      # N % 8
+    assert L.qlora_linear_workspace_bytes(8, 4096, 4096, 129, 0) == 0     # r > 128
+    assert L.qlora_linear_workspace_bytes(8, 4096, 4096, 0, 1) == 0       # r < 1
+    assert L.qlora_lora_grads_workspace_bytes(8192, 11008, 4096, 64) > 0
+
+
+def _fake_weight(rows, cols, base=0x10000):
+    # Aligned fake device addresses: only valid for calls that fail validation.
+    return _capi.NF4WeightStruct(base, base + 0x1000, base + 0x2000, base + 0x3000, rows, cols)
+
+
+def test_validation_rejects_before_launch():
+    L = q.lib()
+    P = ctypes.c_void_p(0x20000)   # aligned, never dereferenced
+    w = _fake_weight(64, 64)
+    # quantize: null input, bad shape, missing workspace
+    assert L.qlora_quantize_nf4(None, ctypes.byref(w), P, 1 << 20, None) == INVALID
+    assert L.qlora_quantize_nf4(ctypes.c_void_p(0x20004), ctypes.byref(w), P, 1 << 20, None) == INVALID
+    bad = _fake_weight(0, 64)
+    assert L.qlora_quantize_nf4(P, ctypes.byref(bad), P, 1 << 20, None) == INVALID
+    assert L.qlora_quantize_nf4(P, ctypes.byref(w), None, 0, None) == WS
+    assert L.qlora_quantize_nf4(P, ctypes.byref(w), P, 1, None) == WS
+    nullw = _capi.NF4WeightStruct(0, 0x11000, 0x12000, 0x13000, 64, 64)
+    assert L.qlora_quantize_nf4(P, ctypes.byref(nullw), P, 1 << 20, None) == INVALID
+    assert L.qlora_dequantize_nf4(None, P, None) == INVALID
+    assert L.qlora_dequantize_nf4(ctypes.byref(w), None, None) == INVALID
+    # linear: K % 64, N % 8, r range, scale, pointers, workspace
+    wk = _fake_weight(64, 100)
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(wk), P, P, 8, 1.0, P, P, None, 0, None) == SHAPE
+    wn = _fake_weight(63, 64)
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(wn), P, P, 8, 1.0, P, P, None, 0, None) == SHAPE
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(w), P, P, 0, 1.0, P, P, None, 0, None) == SHAPE
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(w), P, P, 129, 1.0, P, P, None, 0, None) == SHAPE
+    assert L.qlora_linear_fwd(P, -1, ctypes.byref(w), P, P, 8, 1.0, P, P, None, 0, None) == INVALID
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(w), P, P, 8, float("nan"), P, P, None, 0, None) == INVALID
+    assert L.qlora_linear_fwd(None, 8, ctypes.byref(w), P, P, 8, 1.0, P, P, None, 0, None) == INVALID
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(w), P, P, 8, 1.0, P, None, None, 0, None) == WS
+    assert L.qlora_linear_fwd(P, 8, ctypes.byref(w), P, P, 8, 1.0, P, None, P, 16, None) == WS
+    assert L.qlora_linear_bwd(P, P, P, 8, ctypes.byref(w), P, P, 8, 1.0, P, P, P, None, 0, None) == WS
+    assert L.qlora_linear_bwd(P, P, P, 8, ctypes.byref(wk), P, P, 8, 1.0, P, P, P, P, 1 << 30, None) == SHAPE
+    assert L.qlora_linear_bwd(None, P, P, 8, ctypes.byref(w), P, P, 8, 1.0, P, P, P, P, 1 << 30, None) == INVALID
+    # M = 0 is valid and launches nothing
+    assert L.qlora_linear_fwd(P, 0, ctypes.byref(w), P, P, 8, 1.0, P, P, None, 0, None) == OK
+    assert L.qlora_linear_bwd(P, P, P, 0, ctypes.byref(w), P, P, 8, 1.0, P, P, P, P, 1 << 30, None) == OK
+    assert L.qlora_nf4_matmul_fwd(P, 0, ctypes.byref(w), P, P, 8, 1.0, P, None) == OK
+    assert L.qlora_nf4_matmul_dx(P, 0, ctypes.byref(w), P, P, 8, 1.0, P, None) == OK
+    assert L.qlora_lora_down(P, 0, 64, P, 8, P, None) == OK
+    assert L.qlora_lora_down(P, 4, 60, P, 8, P, None) == SHAPE
+    assert L.qlora_lora_grad_in(P, 4, 60, P, 200, P, None) == SHAPE
+    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 8, 1.0, P, P, None, 0, None) == WS
+    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 0, 1.0, P, P, P, 1 << 30, None) == SHAPE
+    # misaligned weight buffers
+    mis = _capi.NF4WeightStruct(0x10008, 0x11000, 0x12000, 0x13000, 64, 64)
+    assert L.qlora_dequantize_nf4(ctypes.byref(mis), P, None) == INVALID
+    # size overflow
+    huge = _fake_weight(1 << 20, 1 << 20)
+    assert L.qlora_dequantize_nf4(ctypes.byref(huge), P, None) == SHAPE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    W = torch.zeros(64, 64)
+    with pytest.raises(ValueError):
+        q.NF4Weight.quantize(W)

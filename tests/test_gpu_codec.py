@@ -1,0 +1,118 @@
+"""GPU parity of the codec (qlora_quantize_nf4, qlora_dequantize_nf4) with the
+CPU oracle: packed codes, constant codes, scales, mean and the dequantized
+bf16 weights must be bit-identical."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_absmax_amd as q
+import workloads
+from oracle import nf4
+from tests.gpu_util import DEV, bf16_bits, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quantize(w2d):
+    W = to_dev_f32(w2d)
+    qw = q.NF4Weight.quantize(W)
+    torch.cuda.synchronize()
+    return qw
+
+
+def _check(w2d, name):
+    print("codec case", name, w2d.shape, flush=True)
+    qw = _gpu_quantize(w2d)
+    ref = nf4.quantize(w2d)
+    packed = qw.packed.cpu().numpy()
+    code8 = qw.code8.cpu().numpy()
+    c2 = qw.c2.cpu().numpy()
+    mean = qw.mean.cpu().numpy()[0]
+    assert np.array_equal(packed, ref["packed"]), name + ": packed"
+    assert np.array_equal(code8, ref["code8"]), name + ": code8"
+    assert np.array_equal(c2.view(np.uint32), ref["c2"].view(np.uint32)), name + ": c2"
+    assert np.float32(mean).view(np.uint32) == np.float32(ref["mean"]).view(np.uint32), name + ": mean"
+    wt = bf16_bits(qw.dequantize())
+    assert np.array_equal(wt.reshape(-1), nf4.dequantize_q(ref)), name + ": dequant"
+    return qw, ref
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 63), (3, 65), (7, 1001), (257, 64), (64, 4096 + 64), (1, 64 * 257 + 3)])
+def test_codec_odd_shapes(shape):
+    rng = np.random.default_rng(sum(shape))
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    _check(w, "odd%s" % (shape,))
+
+
+def test_codec_linear_1024():
+    cfg = workloads.CONFIGS[0]
+    w = workloads.linear_inputs(cfg, 0)["W"]
+    _check(w, "linear_1024")
+
+
+@pytest.mark.parametrize("li", [0, 4, 6])
+def test_codec_llama7b_shapes(li):
+    cfg = workloads.CONFIGS[1]
+    lin = cfg.linears[li]
+    w = workloads.weight((lin.out_features, lin.in_features), workloads.seed_for(1, 10 * li))
+    _check(w, lin.name)
+
+
+def test_codec_special_blocks():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((40, 1024)) * 0.02).astype(np.float32)
+    flat = w.reshape(-1)
+    flat[0:64] = 0.0                                  # all-zero block
+    flat[64:128] = -0.0                               # all negative-zero block
+    flat[128:192] = np.float32(0.25) * np.sign(flat[128:192])   # +-absmax everywhere
+    flat[192] = np.float32(-3.0)                      # outlier, negative absmax
+    flat[256:320] = np.float32(1e-40)                 # subnormal block
+    flat[320:384] = np.float32(1e30)                  # huge finite values
+    flat[384:448] = nf4.nf4_levels().repeat(4) * np.float32(0.07)  # exact level multiples
+    _check(w, "special_blocks")
+
+
+def test_codec_constant_absmax_zero_scale():
+    rng = np.random.default_rng(6)
+    w = np.sign(rng.standard_normal((64, 512))).astype(np.float32) * np.float32(0.03)
+    qw, ref = _check(w, "constant_absmax")
+    assert np.all(ref["c2"] == 0.0)
+
+
+def test_codec_all_zero():
+    w = np.zeros((128, 256), np.float32)
+    qw, ref = _check(w, "all_zero")
+    assert np.all(bf16_bits(qw.dequantize()) == 0)
+
+
+def test_code_rule_near_every_threshold():
+    # Blocks whose absmax element is exactly +1 or -1, so x = w / c = w: the
+    # other 63 slots sweep every fp32 within 4000 steps of each decision
+    # threshold (and the naive-rounding and exact-tie cases among them).
+    lv = nf4.nf4_levels().astype(np.float64)
+    vals = []
+    for i in range(15):
+        m = np.float32((lv[i] + lv[i + 1]) / 2)
+        k = int(m.view(np.int32)) if m >= 0 else -int((m.view(np.uint32) & np.uint32(0x7FFFFFFF)))
+        keys = np.arange(k - 4000, k + 4001, dtype=np.int64)
+        bits = np.where(keys >= 0, keys, (-keys) | 0x80000000).astype(np.uint32)
+        vals.append(bits.view(np.float32))
+    vals = np.concatenate(vals)
+    vals = vals[np.abs(vals) <= 1.0]
+    nblk = (len(vals) + 62) // 63
+    w = np.zeros((nblk, 64), np.float32)
+    flat = np.zeros(nblk * 63, np.float32)
+    flat[:len(vals)] = vals
+    w[:, 1:] = flat.reshape(nblk, 63)
+    w[:, 0] = np.where(np.arange(nblk) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    _check(w.reshape(1, -1), "threshold_sweep")
+
+
+def test_quantize_is_deterministic():
+    rng = np.random.default_rng(8)
+    w = to_dev_f32((rng.standard_normal((512, 2048)) * 0.02).astype(np.float32))
+    a = q.NF4Weight.quantize(w)
+    b = q.NF4Weight.quantize(w)
+    for x, y in ((a.packed, b.packed), (a.code8, b.code8), (a.c2, b.c2), (a.mean, b.mean)):
+        assert torch.equal(x, y)
