@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA frozen-base linear layer on one MI355X.
+
+Workload (the headline): the seven linears of a LLaMA-7B-shaped decoder
+layer (q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008), weights
+N(0, 0.02) quantized to NF4 with double-quantized constants, 8192 tokens of
+bf16 activations N(0, 1), LoRA r = 64, alpha = 16 on every linear.  One step
+is the forward and the backward (dX, dA, dB) of all seven linears with the
+weights already quantized and every input resident in HBM:
+    T = X A^T;  Y = X deq(W)^T + s T B^T;  G = dY B;
+    dX = dY deq(W) + s G A;  dA = s G^T X;  dB = s dY^T T.
+Metric: algorithmic TFLOP/s = sum over linears of 4 M N K + 6 M r (N + K)
+per step, divided by the step time.
+
+Also reported on the same JSON line:
+  roofline      the dominant kernel (fused dequant matmul), timed with HIP
+                events around each of its launches inside the timed region
+  cpu_baseline  the CPU oracle on a bounded token sample of the same step
+  small_m       forward-only M = 1 / 16 / 64 over 4 weight sets (> the 256 MB
+                Infinity Cache), algorithmic HBM GB/s
+  quantize      quantize throughput on the 7 weights (algorithmic GB/s)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "NF4+LoRA linear fwd+bwd TFLOP/s (7B layer, 8192 tok); small-M dequant GB/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-extras", action="store_true", help="skip small-M and quantize figures")
+    p.add_argument("--cpu-tokens", type=int, default=256, help="token sample for the CPU oracle")
+    return p.parse_args()
+
+
+def linear_flops(M, N, K, r):
+    return 4.0 * M * N * K + 6.0 * M * r * (N + K)
+
+
+def small_m_bytes(M, N, K, r):
+    # packed codes + 8-bit constants + fp32 group scales + mean + X + Y + A + B
+    return N * K / 2 + N * K / 64 + 4 * N * K / 16384 + 4 + 2 * M * K + 2 * M * N + 2 * r * K + 2 * r * N
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device-resident inputs, outputs and workspaces of one linear."""
+
+    def __init__(self, q, torch, workloads, lin, M, r, seed, dev):
+        N, K = lin.out_features, lin.in_features
+        self.name, self.M, self.N, self.K, self.r = lin.name, M, N, K, r
+        W = workloads.device_normal((N, K), workloads.W_STD, seed, dev)
+        self.w = q.NF4Weight.quantize(W)
+        del W
+        bf = torch.bfloat16
+        self.X = workloads.device_normal((M, K), 1.0, seed + 1, dev, bf)
+        self.A = workloads.device_normal((r, K), workloads.LORA_STD, seed + 2, dev, bf)
+        self.B = workloads.device_normal((N, r), workloads.LORA_STD, seed + 3, dev, bf)
+        self.dY = workloads.device_normal((M, N), 1.0, seed + 4, dev, bf)
+        self.Y = torch.empty(M, N, dtype=bf, device=dev)
+        self.T = torch.empty(M, r, dtype=bf, device=dev)
+        self.G = torch.empty(M, r, dtype=bf, device=dev)
+        self.dX = torch.empty(M, K, dtype=bf, device=dev)
+        ws = q.lib().qlora_lora_grads_workspace_bytes(M, N, K, r)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.flops = linear_flops(M, N, K, r)
+        self.fwd_mm_flops = 2.0 * M * N * K + 2.0 * M * r * N
+        self.dx_mm_flops = 2.0 * M * N * K + 2.0 * M * r * K
+
+
+def run_step(q, torch, layers, scale, events=None):
+    for L in layers:
+        q.lora_down(L.X, L.A, scale, out=L.T)
+        if events is not None:
+            events["fwd"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), L))
+            events["fwd"][-1][0].record()
+        q.nf4_matmul_fwd(L.X, L.w, L.T, L.B, out=L.Y)
+        if events is not None:
+            events["fwd"][-1][1].record()
+        q.lora_grad_in(L.dY, L.B, scale, out=L.G)
+        if events is not None:
+            events["dx"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), L))
+            events["dx"][-1][0].record()
+        q.nf4_matmul_dx(L.dY, L.w, L.G, L.A, out=L.dX)
+        if events is not None:
+            events["dx"][-1][1].record()
+        q.lora_grads(L.X, L.dY, L.G, L.T, workspace=L.ws)
+
+
+def cpu_baseline(cfg, tokens):
+    """The oracle (as it stands) on `tokens` tokens of every linear of the step."""
+    import workloads
+    from oracle import linear as olin
+    from oracle import nf4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    total_flops, total_s = 0.0, 0.0
+    for li, lin in enumerate(cfg.linears):
+        d = workloads.linear_inputs(cfg, li, tokens=tokens)
+        qd = nf4.quantize(d["W"])          # weights are pre-quantized in the step: untimed
+        t0 = time.perf_counter()
+        wt = nf4.dequantize_q(qd).reshape(d["N"], d["K"])
+        olin.linear_fwd(d["X"], wt, d["A"], d["B"], cfg.scale)
+        olin.linear_bwd(d["dY"], d["X"], wt, d["A"], d["B"], cfg.scale)
+        total_s += time.perf_counter() - t0
+        total_flops += linear_flops(tokens, d["N"], d["K"], d["r"])
+    return dict(value=total_flops / total_s / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample="fp64 NumPy oracle fwd+bwd of all 7 linears (dequantize + products) on %d of the 8192 "
+                       "tokens, %.1f s; rate = algorithmic FLOP / time" % (tokens, total_s))
+
+
+def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
+    """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache)."""
+    r = cfg.rank
+    sets = []
+    for s in range(4):
+        ws = []
+        for li, lin in enumerate(cfg.linears):
+            W = workloads.device_normal((lin.out_features, lin.in_features), workloads.W_STD,
+                                        90000 + 100 * s + li, dev)
+            ws.append(q.NF4Weight.quantize(W))
+            del W
+        sets.append(ws)
+    out = {}
+    for M in cfg.small_m:
+        lin_in = []
+        for li, lin in enumerate(cfg.linears):
+            N, K = lin.out_features, lin.in_features
+            X = workloads.device_normal((M, K), 1.0, 91000 + li, dev, torch.bfloat16)
+            A = workloads.device_normal((r, K), workloads.LORA_STD, 92000 + li, dev, torch.bfloat16)
+            B = workloads.device_normal((N, r), workloads.LORA_STD, 93000 + li, dev, torch.bfloat16)
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+            lin_in.append((X, A, B, Y, T))
+        nbytes = sum(small_m_bytes(M, l.out_features, l.in_features, r) for l in cfg.linears)
+
+        def one_layer(ws):
+            for (X, A, B, Y, T), w in zip(lin_in, ws):
+                q.linear_fwd(X, w, A, B, cfg.scale, T_out=T)
+
+        for ws in sets:
+            one_layer(ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for ws in sets:
+                one_layer(ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out["M%d" % M] = dict(us_per_layer=round(us, 2), bytes_per_layer=int(nbytes), GBps=round(gbs, 1),
+                              frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def quantize_bench(q, torch, workloads, cfg, dev, reps=5):
+    Ws = [workloads.device_normal((l.out_features, l.in_features), workloads.W_STD, 95000 + i, dev)
+          for i, l in enumerate(cfg.linears)]
+    for W in Ws:
+        q.NF4Weight.quantize(W)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for W in Ws:
+            q.NF4Weight.quantize(W)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    params = sum(W.numel() for W in Ws)
+    nbytes = params * (4 + 0.5 + 1 / 64 + 4 / 16384)
+    del Ws
+    torch.cuda.empty_cache()
+    return dict(ms_per_layer=round(ms, 3), params=int(params), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                note="includes workspace allocation by the Python binding")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_nf4_quantized_absmax_amd as q
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    cfg = workloads.CONFIGS[1]
+    scale = cfg.scale
+    log("building inputs for", cfg.name)
+    layers = [Layer(q, torch, workloads, lin, cfg.tokens, cfg.rank, 1000 * cfg.index + 10 * i, dev)
+              for i, lin in enumerate(cfg.linears)]
+    step_flops = sum(L.flops for L in layers)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_step(q, torch, layers, scale)
+    torch.cuda.synchronize()
+    log("warmup done; timing %d steps" % args.steps)
+
+    events = {"fwd": [], "dx": []}
+    t0 = time.perf_counter()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        run_step(q, torch, layers, scale, events)
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = g0.elapsed_time(g1) / args.steps
+    tflops = step_flops / (ms_step * 1e-3) / 1e12
+    log("step %.3f ms  %.1f TFLOP/s (wall %.3f s)" % (ms_step, tflops, wall))
+
+    kern = {}
+    for key, evs in events.items():
+        tot_ms = sum(a.elapsed_time(b) for a, b, _ in evs)
+        flops = sum((L.fwd_mm_flops if key == "fwd" else L.dx_mm_flops) for _, _, L in evs)
+        kern[key] = dict(launches=len(evs), avg_us=tot_ms * 1e3 / len(evs),
+                         flops_per_launch=flops / len(evs), total_ms=tot_ms)
+    dom_key = max(kern, key=lambda k: kern[k]["total_ms"])
+    dom = kern[dom_key]
+    achieved = dom["flops_per_launch"] / (dom["avg_us"] * 1e-6) / 1e12
+    roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                    kernel="k_matmul_fwd" if dom_key == "fwd" else "k_matmul_dx",
+                    avg_launch_us=round(dom["avg_us"], 2),
+                    flops_per_launch=dom["flops_per_launch"])
+    other = {k: dict(avg_us=round(v["avg_us"], 2), TFLOPs=round(v["flops_per_launch"] / (v["avg_us"] * 1e-6) / 1e12, 1),
+                     share_of_step=round(v["total_ms"] / args.steps / ms_step, 3)) for k, v in kern.items()}
+
+    extras = {}
+    if not args.no_extras:
+        del layers
+        torch.cuda.empty_cache()
+        log("small-M forward")
+        extras["small_m"] = small_m_bench(q, torch, workloads, workloads.CONFIGS[2], dev)
+        log("quantize")
+        extras["quantize"] = quantize_bench(q, torch, workloads, cfg, dev)
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu oracle baseline on %d tokens" % args.cpu_tokens)
+        cpu = cpu_baseline(cfg, args.cpu_tokens)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ; N(0,1) bf16 activations)",
+        "config": {"workload": "llama7b_layer_7linears_fwd_bwd", "tokens": cfg.tokens, "rank": cfg.rank,
+                   "alpha": cfg.alpha, "step_flops": step_flops,
+                   "shapes": "q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008 (N x K)",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": other,
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

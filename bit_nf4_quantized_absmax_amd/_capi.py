@@ -58,13 +58,12 @@ _SIGS = {
     "qlora_linear_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
-    "qlora_lora_down": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _vp, _vp]),
-    "qlora_nf4_matmul_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp]),
-    "qlora_lora_grad_in": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _vp, _vp]),
-    "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_lora_down": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_nf4_matmul_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
+    "qlora_lora_grad_in": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
     "qlora_lora_grads_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
-    "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _sz,
-                                        _vp]),
+    "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
 }
 
 

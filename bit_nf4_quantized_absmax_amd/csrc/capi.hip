@@ -122,43 +122,45 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
   return is_bwd ? bwd_ws(M, N, K, r).total : fwd_ws(M, r);
 }
 
-int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r, uint16_t *T,
-                    void *stream) {
-  if (M < 0 || K < 8 || K % 8 || r < 1 || r > 128) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_UNSUPPORTED_SHAPE;
+int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r, float scale,
+                    uint16_t *T, void *stream) {
+  if (M < 0 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
+  if (K < 8 || K % 8 || r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > kMaxElems / K) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(T)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
-  return from_hip(launch_lora_down(X, static_cast<int>(M), static_cast<int>(K), A, r, T,
+  return from_hip(launch_lora_down(X, static_cast<int>(M), static_cast<int>(K), A, r, scale, T,
                                    static_cast<hipStream_t>(stream)));
 }
 
-int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r, uint16_t *G,
-                       void *stream) {
-  if (M < 0 || N < 8 || N % 8 || r < 1 || r > 128) return M < 0 ? QLORA_ERR_INVALID_ARG : QLORA_ERR_UNSUPPORTED_SHAPE;
+int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r, float scale,
+                       uint16_t *G, void *stream) {
+  if (M < 0 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
+  if (N < 8 || N % 8 || r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > kMaxElems / N) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!bf16_ok(dY) || !bf16_ok(B) || !bf16_ok(G)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
-  return from_hip(launch_lora_grad_in(dY, static_cast<int>(M), static_cast<int>(N), B, r, G,
+  return from_hip(launch_lora_grad_in(dY, static_cast<int>(M), static_cast<int>(N), B, r, scale, G,
                                       static_cast<hipStream_t>(stream)));
 }
 
 int qlora_nf4_matmul_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *T,
-                         const uint16_t *B, int32_t r, float scale, uint16_t *Y, void *stream) {
-  int st = check_linear_shape(M, W, r, scale);
+                         const uint16_t *B, int32_t r, uint16_t *Y, void *stream) {
+  int st = check_linear_shape(M, W, r, 1.0f);
   if (st) return st;
   if (!bf16_ok(X) || !bf16_ok(T) || !bf16_ok(B) || !bf16_ok(Y)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
-  return from_hip(launch_matmul_fwd(X, static_cast<int>(M), view_of(W), T, B, r, scale, Y,
+  return from_hip(launch_matmul_fwd(X, static_cast<int>(M), view_of(W), T, B, r, Y,
                                     static_cast<hipStream_t>(stream)));
 }
 
 int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W, const uint16_t *G,
-                        const uint16_t *A, int32_t r, float scale, uint16_t *dX, void *stream) {
-  int st = check_linear_shape(M, W, r, scale);
+                        const uint16_t *A, int32_t r, uint16_t *dX, void *stream) {
+  int st = check_linear_shape(M, W, r, 1.0f);
   if (st) return st;
   if (!bf16_ok(dY) || !bf16_ok(G) || !bf16_ok(A) || !bf16_ok(dX)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
-  return from_hip(launch_matmul_dx(dY, static_cast<int>(M), view_of(W), G, A, r, scale, dX,
+  return from_hip(launch_matmul_dx(dY, static_cast<int>(M), view_of(W), G, A, r, dX,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -169,9 +171,9 @@ size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t
 }
 
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, const uint16_t *T, int64_t M,
-                     int64_t N, int64_t K, int32_t r, float scale, uint16_t *dA, uint16_t *dB, void *ws,
-                     size_t ws_bytes, void *stream) {
-  if (M < 0 || N < 1 || K < 1 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
+                     int64_t N, int64_t K, int32_t r, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
+                     void *stream) {
+  if (M < 0 || N < 1 || K < 1) return QLORA_ERR_INVALID_ARG;
   if (r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > 0 && M > kMaxElems / std::max(N, K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
@@ -183,11 +185,11 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int m = static_cast<int>(M);
   if (dA) {
-    hipError_t e = launch_lora_grad_w(X, G, m, static_cast<int>(K), r, scale, true, dA, ws, s);
+    hipError_t e = launch_lora_grad_w(X, G, m, static_cast<int>(K), r, true, dA, ws, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dB) {
-    hipError_t e = launch_lora_grad_w(dY, T, m, static_cast<int>(N), r, scale, false, dB,
+    hipError_t e = launch_lora_grad_w(dY, T, m, static_cast<int>(N), r, false, dB,
                                       static_cast<char *>(ws) + pa, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
@@ -209,9 +211,9 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const NF4View v = view_of(W);
   const int m = static_cast<int>(M);
-  hipError_t e = launch_lora_down(X, m, v.K, A, r, T, s);
+  hipError_t e = launch_lora_down(X, m, v.K, A, r, scale, T, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  return from_hip(launch_matmul_fwd(X, m, v, T, B, r, scale, Y, s));
+  return from_hip(launch_matmul_fwd(X, m, v, T, B, r, Y, s));
 }
 
 int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,
@@ -234,25 +236,25 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
   void *pb = base + L.t + L.g + L.pa;
   hipError_t e = hipSuccess;
   if (dX || dA) {
-    e = launch_lora_grad_in(dY, m, v.N, B, r, G, s);
+    e = launch_lora_grad_in(dY, m, v.N, B, r, scale, G, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dX) {
-    e = launch_matmul_dx(dY, m, v, G, A, r, scale, dX, s);
+    e = launch_matmul_dx(dY, m, v, G, A, r, dX, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dA) {
-    e = launch_lora_grad_w(X, G, m, v.K, r, scale, true, dA, pa, s);
+    e = launch_lora_grad_w(X, G, m, v.K, r, true, dA, pa, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dB) {
     const uint16_t *Tu = T;
     if (!Tu) {
-      e = launch_lora_down(X, m, v.K, A, r, Tw, s);
+      e = launch_lora_down(X, m, v.K, A, r, scale, Tw, s);
       if (e != hipSuccess) return QLORA_ERR_HIP;
       Tu = Tw;
     }
-    e = launch_lora_grad_w(dY, Tu, m, v.N, r, scale, false, dB, pb, s);
+    e = launch_lora_grad_w(dY, Tu, m, v.N, r, false, dB, pb, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   return QLORA_OK;

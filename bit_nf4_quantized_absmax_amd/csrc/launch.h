@@ -27,28 +27,24 @@ struct NF4View {
   int K;  // columns (input features), multiple of 64
 };
 
-// ---- large-M matmuls -----------------------------------------------------------
+// ---- large-M matmuls (T and G already carry the LoRA scale) ---------------------
+// Y [M, N] = X deq(W)^T + T B^T
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
-                             const uint16_t *B, int r, float scale, uint16_t *Y, hipStream_t s);
+                             const uint16_t *B, int r, uint16_t *Y, hipStream_t s);
+// dX [M, K] = dY deq(W) + G A
 hipError_t launch_matmul_dx(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
-                            const uint16_t *A, int r, float scale, uint16_t *dX, hipStream_t s);
+                            const uint16_t *A, int r, uint16_t *dX, hipStream_t s);
 
 // ---- LoRA skinny products ------------------------------------------------------
-// T [M, r] = X [M, K] A^T  (A [r, K])
-hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, uint16_t *T,
-                            hipStream_t s);
-// G [M, r] = dY [M, N] B  (B [N, r])
-hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r,
+// T [M, r] = scale X [M, K] A^T  (A [r, K])
+hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, float scale,
+                            uint16_t *T, hipStream_t s);
+// G [M, r] = scale dY [M, N] B  (B [N, r])
+hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r, float scale,
                                uint16_t *G, hipStream_t s);
-// out = scale * P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB).
+// out = P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB).
 size_t lora_grad_ws_bytes(int M, int D, int r);
-hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, float scale,
-                              bool out_r_major, uint16_t *out, void *ws, hipStream_t s);
-
-// ---- small-M forward ------------------------------------------------------------
-int small_m_max();
-hipError_t launch_small_m_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *A,
-                              const uint16_t *B, int r, float scale, uint16_t *Y, uint16_t *T,
-                              hipStream_t s);
+hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
+                              uint16_t *out, void *ws, hipStream_t s);
 
 }  // namespace qlora

@@ -5,12 +5,14 @@
 // explained", The problem and How it works; creativeworksofknowledge.com,
 // "QLoRA: Fine-Tune 70B on One GPU", Code: r, lora_alpha).  With A [r, K],
 // B [N, r]:
-//   k_skinny_nt<false>   T = X A^T     (contraction over K, both K-contiguous)
-//   k_skinny_nt<true>    G = dY B      (contraction over N; B read transposed)
-//   k_grad_partial       s P^T Q over an M-slice -> fp32 partials
+//   k_skinny_nt<false>   T = s X A^T   (contraction over K, both K-contiguous)
+//   k_skinny_nt<true>    G = s dY B    (contraction over N; B read transposed)
+//   k_grad_partial       P^T Q over an M-slice -> fp32 partials
 //   k_grad_reduce        fixed-order sum of the partials, bf16 out
-// with (P, Q) = (X, G) for dA [r, K] and (dY, T) for dB [N, r].  These are
-// streaming products: each reads its wide operand (X or dY) once.
+// with (P, Q) = (X, G) for dA = s G0^T X [r, K] and (dY, T) for
+// dB = s dY^T T0 [N, r], where T0, G0 are the unscaled products: the scale
+// s = alpha / r is applied once, in fp32, before T and G are rounded to bf16.
+// These are streaming products: each reads its wide operand (X or dY) once.
 #include <algorithm>
 
 #include "common.h"
@@ -21,14 +23,14 @@ namespace qlora {
 constexpr int kSkThreads = 512;   // 8 waves, each a slice of the contraction
 constexpr int kSkRows = 32;       // output rows per workgroup
 
-// out[m][j] = sum_k L[m][k] R(j, k) for m in a 32-row tile, j < r, where
+// out[m][j] = scale * sum_k L[m][k] R(j, k) for m in a 32-row tile, j < r, where
 // R(j, k) = Rm[j * ldr + k] (kTransR = false, Rm = A [r, K]) or
 // R(j, k) = Rm[k * r + j] (kTransR = true, Rm = B [N, r]).
 // Wave w takes contraction steps of 32 with index w, w + 8, ...; the 8 wave
 // partials are summed in LDS in wave order (deterministic).
 template <bool kTransR, int kRP>
 __global__ __launch_bounds__(kSkThreads) void k_skinny_nt(const uint16_t *__restrict__ L, int M, int Kc,
-                                                          const uint16_t *__restrict__ Rm, int r,
+                                                          const uint16_t *__restrict__ Rm, int r, float scale,
                                                           uint16_t *__restrict__ out) {
   constexpr int kJB = kRP / 16;
   __shared__ float red[8][kSkRows][kRP + 1];
@@ -90,33 +92,33 @@ __global__ __launch_bounds__(kSkThreads) void k_skinny_nt(const uint16_t *__rest
     float s = red[0][row][j];
 #pragma unroll
     for (int w = 1; w < 8; ++w) s += red[w][row][j];
-    if (m0 + row < M && j < r) out[static_cast<int64_t>(m0 + row) * r + j] = f32_to_bf16(s);
+    if (m0 + row < M && j < r) out[static_cast<int64_t>(m0 + row) * r + j] = f32_to_bf16(s * scale);
   }
 }
 
 template <bool kTransR>
-static hipError_t launch_skinny(const uint16_t *L, int M, int Kc, const uint16_t *R, int r, uint16_t *out,
-                                hipStream_t s) {
+static hipError_t launch_skinny(const uint16_t *L, int M, int Kc, const uint16_t *R, int r, float scale,
+                                uint16_t *out, hipStream_t s) {
   const dim3 grid((M + kSkRows - 1) / kSkRows);
   if (r <= 64)
-    hipLaunchKernelGGL((k_skinny_nt<kTransR, 64>), grid, dim3(kSkThreads), 0, s, L, M, Kc, R, r, out);
+    hipLaunchKernelGGL((k_skinny_nt<kTransR, 64>), grid, dim3(kSkThreads), 0, s, L, M, Kc, R, r, scale, out);
   else
-    hipLaunchKernelGGL((k_skinny_nt<kTransR, 128>), grid, dim3(kSkThreads), 0, s, L, M, Kc, R, r, out);
+    hipLaunchKernelGGL((k_skinny_nt<kTransR, 128>), grid, dim3(kSkThreads), 0, s, L, M, Kc, R, r, scale, out);
   return hipGetLastError();
 }
 
-hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, uint16_t *T,
+hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, float scale, uint16_t *T,
                             hipStream_t s) {
-  return launch_skinny<false>(X, M, K, A, r, T, s);
+  return launch_skinny<false>(X, M, K, A, r, scale, T, s);
 }
 
-hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r, uint16_t *G,
-                               hipStream_t s) {
-  return launch_skinny<true>(dY, M, N, B, r, G, s);
+hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r, float scale,
+                               uint16_t *G, hipStream_t s) {
+  return launch_skinny<true>(dY, M, N, B, r, scale, G, s);
 }
 
 // ---------------------------------------------------------------------------
-// dA / dB: out = scale * P^T Q, P [M, D], Q [M, r].
+// dA / dB: out = P^T Q, P [M, D], Q [M, r] (Q already carries the scale).
 // Workgroup (tile d0 .. d0+63, split sp) sums m in its slice of M in steps
 // of 64 rows: P and Q tiles go to LDS row-major and are read transposed into
 // the MFMA operands (8 consecutive m per lane).  4 waves, wave w owns
@@ -196,15 +198,14 @@ __global__ __launch_bounds__(kGrThreads) void k_grad_partial(const uint16_t *__r
 
 template <int kRP>
 __global__ __launch_bounds__(256) void k_grad_reduce(const float *__restrict__ part, int splits, int D, int dpad,
-                                                     int r, float scale, bool out_r_major,
-                                                     uint16_t *__restrict__ out) {
+                                                     int r, bool out_r_major, uint16_t *__restrict__ out) {
   const int64_t total = static_cast<int64_t>(D) * r;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * 256) {
     const int d = static_cast<int>(idx / r), j = static_cast<int>(idx % r);
     float s = 0.f;
     for (int sp = 0; sp < splits; ++sp) s += part[(static_cast<int64_t>(sp) * dpad + d) * kRP + j];
-    const uint16_t v = f32_to_bf16(s * scale);
+    const uint16_t v = f32_to_bf16(s);
     if (out_r_major)
       out[static_cast<int64_t>(j) * D + d] = v;
     else
@@ -218,8 +219,8 @@ size_t lora_grad_ws_bytes(int M, int D, int r) {
   return static_cast<size_t>(grad_splits(M, D)) * dt * kGrD * rp * sizeof(float);
 }
 
-hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, float scale,
-                              bool out_r_major, uint16_t *out, void *ws, hipStream_t s) {
+hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
+                              uint16_t *out, void *ws, hipStream_t s) {
   const int sp = grad_splits(M, D);
   const int dt = (D + kGrD - 1) / kGrD;
   const int msteps = (M + kGrM - 1) / kGrM;
@@ -230,12 +231,12 @@ hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D
   if (r <= 64) {
     hipLaunchKernelGGL(k_grad_partial<64>, dim3(dt, sp), dim3(kGrThreads), 0, s, P, Q, M, D, r, rows_per_split,
                        part);
-    hipLaunchKernelGGL(k_grad_reduce<64>, dim3(rgrid), dim3(256), 0, s, part, sp, D, dt * kGrD, r, scale,
+    hipLaunchKernelGGL(k_grad_reduce<64>, dim3(rgrid), dim3(256), 0, s, part, sp, D, dt * kGrD, r,
                        out_r_major, out);
   } else {
     hipLaunchKernelGGL(k_grad_partial<128>, dim3(dt, sp), dim3(kGrThreads), 0, s, P, Q, M, D, r,
                        rows_per_split, part);
-    hipLaunchKernelGGL(k_grad_reduce<128>, dim3(rgrid), dim3(256), 0, s, part, sp, D, dt * kGrD, r, scale,
+    hipLaunchKernelGGL(k_grad_reduce<128>, dim3(rgrid), dim3(256), 0, s, part, sp, D, dt * kGrD, r,
                        out_r_major, out);
   }
   return hipGetLastError();

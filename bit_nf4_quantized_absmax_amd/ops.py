@@ -117,7 +117,7 @@ def _lin_checks(X, w, A, B, r_expect=None):
 
 
 def linear_fwd(X, w, A, B, scale, T_out=None):
-    """Y = X deq(W)^T + scale (X A^T) B^T; returns (Y, T) with T = X A^T [M, r]."""
+    """Y = X deq(W)^T + scale (X A^T) B^T; returns (Y, T) with T = scale X A^T [M, r]."""
     M, N, K, r = _lin_checks(X, w, A, B)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
     T = T_out if T_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
@@ -129,7 +129,8 @@ def linear_fwd(X, w, A, B, scale, T_out=None):
 
 
 def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=True, workspace=None):
-    """Returns (dX, dA, dB) (None where not requested); T may be None (recomputed)."""
+    """Returns (dX, dA, dB) (None where not requested); T = scale X A^T as
+    returned by linear_fwd, or None (recomputed)."""
     M, N, K, r = _lin_checks(X, w, A, B)
     _need(dY, torch.bfloat16, "dY", (M, N))
     if T is not None:
@@ -149,17 +150,19 @@ def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=Tru
 
 # ---- the individual steps ------------------------------------------------------
 
-def lora_down(X, A, out=None):
+def lora_down(X, A, scale, out=None):
+    """T = scale X A^T."""
     M, K = X.shape
     r = A.shape[0]
     _need(X, torch.bfloat16, "X")
     _need(A, torch.bfloat16, "A", (r, K))
     T = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
-    check(lib().qlora_lora_down(_ptr(X), M, K, _ptr(A), r, _ptr(T), _stream(X)), "qlora_lora_down")
+    check(lib().qlora_lora_down(_ptr(X), M, K, _ptr(A), r, float(scale), _ptr(T), _stream(X)), "qlora_lora_down")
     return T
 
 
-def nf4_matmul_fwd(X, w, T, B, scale, out=None):
+def nf4_matmul_fwd(X, w, T, B, out=None):
+    """Y = X deq(W)^T + T B^T (T = scale X A^T)."""
     M = X.shape[0]
     r = B.shape[1]
     _need(X, torch.bfloat16, "X", (M, w.cols))
@@ -167,22 +170,25 @@ def nf4_matmul_fwd(X, w, T, B, scale, out=None):
     _need(B, torch.bfloat16, "B", (w.rows, r))
     Y = out if out is not None else torch.empty(M, w.rows, dtype=torch.bfloat16, device=X.device)
     st = w.struct()
-    check(lib().qlora_nf4_matmul_fwd(_ptr(X), M, ctypes.byref(st), _ptr(T), _ptr(B), r, float(scale), _ptr(Y),
-                                     _stream(X)), "qlora_nf4_matmul_fwd")
+    check(lib().qlora_nf4_matmul_fwd(_ptr(X), M, ctypes.byref(st), _ptr(T), _ptr(B), r, _ptr(Y), _stream(X)),
+          "qlora_nf4_matmul_fwd")
     return Y
 
 
-def lora_grad_in(dY, B, out=None):
+def lora_grad_in(dY, B, scale, out=None):
+    """G = scale dY B."""
     M, N = dY.shape
     r = B.shape[1]
     _need(dY, torch.bfloat16, "dY")
     _need(B, torch.bfloat16, "B", (N, r))
     G = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=dY.device)
-    check(lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(B), r, _ptr(G), _stream(dY)), "qlora_lora_grad_in")
+    check(lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(B), r, float(scale), _ptr(G), _stream(dY)),
+          "qlora_lora_grad_in")
     return G
 
 
-def nf4_matmul_dx(dY, w, G, A, scale, out=None):
+def nf4_matmul_dx(dY, w, G, A, out=None):
+    """dX = dY deq(W) + G A (G = scale dY B)."""
     M = dY.shape[0]
     r = A.shape[0]
     _need(dY, torch.bfloat16, "dY", (M, w.rows))
@@ -190,12 +196,13 @@ def nf4_matmul_dx(dY, w, G, A, scale, out=None):
     _need(A, torch.bfloat16, "A", (r, w.cols))
     dX = out if out is not None else torch.empty(M, w.cols, dtype=torch.bfloat16, device=dY.device)
     st = w.struct()
-    check(lib().qlora_nf4_matmul_dx(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, float(scale), _ptr(dX),
-                                    _stream(dY)), "qlora_nf4_matmul_dx")
+    check(lib().qlora_nf4_matmul_dx(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, _ptr(dX), _stream(dY)),
+          "qlora_nf4_matmul_dx")
     return dX
 
 
-def lora_grads(X, dY, G, T, scale, need_dA=True, need_dB=True, workspace=None):
+def lora_grads(X, dY, G, T, need_dA=True, need_dB=True, workspace=None):
+    """dA = G^T X, dB = dY^T T (G and T carry the scale)."""
     M, K = X.shape
     N = dY.shape[1]
     r = G.shape[1]
@@ -204,8 +211,8 @@ def lora_grads(X, dY, G, T, scale, need_dA=True, need_dB=True, workspace=None):
     dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
     ws_bytes = lib().qlora_lora_grads_workspace_bytes(M, N, K, r)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(G), _ptr(T), M, N, K, r, float(scale), _ptr(dA),
-                                 _ptr(dB), _ptr(ws), ws_bytes, _stream(X)), "qlora_lora_grads")
+    check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(G), _ptr(T), M, N, K, r, _ptr(dA), _ptr(dB), _ptr(ws),
+                                 ws_bytes, _stream(X)), "qlora_lora_grads")
     return dA, dB
 
 

@@ -110,8 +110,9 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
 
 /* Forward: Y [M, N] = X [M, K] deq(W)^T + scale (X A^T) B^T.
  *   X [M, K], A [r, K], B [N, r], Y [M, N]: bf16.  W: N x K NF4 weight.
- *   T_out [M, r] (nullable): receives T = X A^T in bf16 for reuse in the
- *   backward pass; when NULL, T lives in the workspace.
+ *   T_out [M, r] (nullable): receives T = scale X A^T in bf16 (the LoRA
+ *   intermediate with the scale applied once in fp32 before rounding) for
+ *   reuse in the backward pass; when NULL, T lives in the workspace.
  * Requires K % 64 == 0 (blocks never straddle rows), 1 <= r <= 128, M >= 0
  * (M = 0 launches nothing), N >= 1.  Pages: automatone.win, "QLoRA paper
  * explained", How it works; creativeworksofknowledge.com, "QLoRA: Fine-Tune
@@ -120,8 +121,8 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
                      const uint16_t *A, const uint16_t *B, int32_t r, float scale,
                      uint16_t *Y, uint16_t *T_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Backward: given dY [M, N], X [M, K] and optionally T = X A^T [M, r]
- * (NULL: recomputed), writes
+/* Backward: given dY [M, N], X [M, K] and optionally T = scale X A^T [M, r]
+ * as written by qlora_linear_fwd (NULL: recomputed), writes
  *   dX [M, K] = dY deq(W) + scale (dY B) A        (nullable: skipped)
  *   dA [r, K] = scale (dY B)^T X                  (nullable: skipped)
  *   dB [N, r] = scale dY^T T                      (nullable: skipped)
@@ -137,36 +138,37 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
 
 /* ---- The individual steps of the two passes (same conventions) ---------- */
 
-/* T [M, r] = X [M, K] A^T, A [r, K]; bf16 in, bf16 out (fp32 accumulation). */
+/* T [M, r] = scale X [M, K] A^T, A [r, K]; bf16 in, fp32 accumulation, the
+ * scale applied in fp32 before the single rounding to bf16.  K % 8 == 0. */
 int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r,
-                    uint16_t *T, void *stream);
+                    float scale, uint16_t *T, void *stream);
 
-/* Y [M, N] = X deq(W)^T + scale T B^T, with T [M, r] given (the fused
+/* Y [M, N] = X deq(W)^T + T B^T with T = scale X A^T [M, r] given: the fused
  * dequant-matmul with the LoRA up-projection folded in as one extra
- * contraction step).  No workspace. */
+ * contraction step.  No workspace. */
 int qlora_nf4_matmul_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
-                         const uint16_t *T, const uint16_t *B, int32_t r, float scale,
-                         uint16_t *Y, void *stream);
+                         const uint16_t *T, const uint16_t *B, int32_t r, uint16_t *Y,
+                         void *stream);
 
-/* G [M, r] = dY [M, N] B, B [N, r]. */
+/* G [M, r] = scale dY [M, N] B, B [N, r] (scale applied before rounding). */
 int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r,
-                       uint16_t *G, void *stream);
+                       float scale, uint16_t *G, void *stream);
 
-/* dX [M, K] = dY deq(W) + scale G A, G [M, r] given.  No workspace. */
+/* dX [M, K] = dY deq(W) + G A with G = scale dY B [M, r] given.  No workspace. */
 int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W,
-                        const uint16_t *G, const uint16_t *A, int32_t r, float scale,
-                        uint16_t *dX, void *stream);
+                        const uint16_t *G, const uint16_t *A, int32_t r, uint16_t *dX,
+                        void *stream);
 
 /* Workspace bytes for qlora_lora_grads. */
 size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 
-/* dA [r, K] = scale G^T X and/or dB [N, r] = scale dY^T T (either output
- * may be NULL), reduced over M in fp32 split-M partials plus a fixed-order
- * second pass.  G/X are needed for dA, dY/T for dB. */
+/* dA [r, K] = G^T X and/or dB [N, r] = dY^T T, with G = scale dY B and
+ * T = scale X A^T as produced above (either output may be NULL), reduced
+ * over M in fp32 split-M partials plus a fixed-order second pass.  G and X
+ * are needed for dA, dY and T for dB. */
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
                      const uint16_t *T, int64_t M, int64_t N, int64_t K, int32_t r,
-                     float scale, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
-                     void *stream);
+                     uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

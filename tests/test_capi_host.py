@@ -94,13 +94,15 @@ def test_validation_rejects_before_launch():
     # M = 0 is valid and launches nothing
     assert L.qlora_linear_fwd(P, 0, ctypes.byref(w), P, P, 8, 1.0, P, P, None, 0, None) == OK
     assert L.qlora_linear_bwd(P, P, P, 0, ctypes.byref(w), P, P, 8, 1.0, P, P, P, P, 1 << 30, None) == OK
-    assert L.qlora_nf4_matmul_fwd(P, 0, ctypes.byref(w), P, P, 8, 1.0, P, None) == OK
-    assert L.qlora_nf4_matmul_dx(P, 0, ctypes.byref(w), P, P, 8, 1.0, P, None) == OK
-    assert L.qlora_lora_down(P, 0, 64, P, 8, P, None) == OK
-    assert L.qlora_lora_down(P, 4, 60, P, 8, P, None) == SHAPE
-    assert L.qlora_lora_grad_in(P, 4, 60, P, 200, P, None) == SHAPE
-    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 8, 1.0, P, P, None, 0, None) == WS
-    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 0, 1.0, P, P, P, 1 << 30, None) == SHAPE
+    assert L.qlora_nf4_matmul_fwd(P, 0, ctypes.byref(w), P, P, 8, P, None) == OK
+    assert L.qlora_nf4_matmul_dx(P, 0, ctypes.byref(w), P, P, 8, P, None) == OK
+    assert L.qlora_nf4_matmul_fwd(P, 8, ctypes.byref(wk), P, P, 8, P, None) == SHAPE
+    assert L.qlora_lora_down(P, 0, 64, P, 8, 1.0, P, None) == OK
+    assert L.qlora_lora_down(P, 4, 60, P, 8, 1.0, P, None) == SHAPE
+    assert L.qlora_lora_down(P, 4, 64, P, 8, float("inf"), P, None) == INVALID
+    assert L.qlora_lora_grad_in(P, 4, 60, P, 200, 1.0, P, None) == SHAPE
+    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 8, P, P, None, 0, None) == WS
+    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 0, P, P, P, 1 << 30, None) == SHAPE
     # misaligned weight buffers
     mis = _capi.NF4WeightStruct(0x10008, 0x11000, 0x12000, 0x13000, 64, 64)
     assert L.qlora_dequantize_nf4(ctypes.byref(mis), P, None) == INVALID
