@@ -59,6 +59,20 @@ constexpr int kWaitVm0Lgkm0 = 0x0070;       // vmcnt(0) lgkmcnt(0)
 constexpr int kWaitVm3Lgkm0 = 0x0073;       // all but the 3 refill loads of a forward step
 constexpr int kWaitVm6Lgkm0 = 0x0076;       // all but the 6 refill loads of a dX step
 
+// Wave roles.  The two wave groups must share every SIMD (one wave of each per
+// SIMD) so that one group's MFMAs overlap the other group's expansion; waves of
+// a workgroup are placed on the 4 SIMDs round-robin (wave w on SIMD w % 4), so
+// waves 0-3 form group 0 and waves 4-7 group 1.
+#ifndef QLORA_GROUP_OF_WAVE
+#define QLORA_GROUP_OF_WAVE(w) ((w) >> 2)
+#define QLORA_INDEX_IN_GROUP(w) ((w) & 3)
+#endif
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int wave_group() { return QLORA_GROUP_OF_WAVE(wave_id()); }
+__device__ __forceinline__ int wave_in_group() { return QLORA_INDEX_IN_GROUP(wave_id()); }
+// thread index 0..255 within its group
+__device__ __forceinline__ int thread_in_group() { return wave_in_group() * 64 + (threadIdx.x & 63); }
+
 // Byte offset of 16-byte chunk `chunk` (0..7) of row `row` in a swizzled stage.
 __device__ __forceinline__ int xswz(int row, int chunk) {
   return row * 128 + 16 * (chunk ^ ((row & 7) ^ ((row >> 3) & 1)));
@@ -93,21 +107,25 @@ __device__ __forceinline__ void dma_left(uint8_t *stage, const uint16_t *src, in
 // Workgroup barrier without a memory-model fence: waits for this wave's LDS
 // operations (and, with kWaitVm*, for its DMA loads) and then s_barrier.  A
 // fence would also wait for every outstanding DMA and prefetch load.  The
-// signal fences stop the compiler from moving memory accesses across it.
+// signal fences stop the compiler from moving memory accesses across it, and
+// the scheduling barriers keep each phase its own scheduling region (no
+// instruction of one phase is moved into another).
 template <int kWait>
 __device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWait);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One 64-wide contraction step of this wave's 128 x 64 block.
 // MFMA 32x32x16: lane l supplies row (l & 31) of A and column (l & 31) of B,
 // with contraction elements 8 (l >> 5) .. +7 of each 16-wide sub-step.
 __device__ __forceinline__ void mfma_step(const uint8_t *xs, const uint8_t *ws, f32x16_t (&acc)[4][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave_group(), wn = wave_in_group();
   const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -217,7 +235,7 @@ struct FwdPack {
   uint32_t code;
   float c2;
   __device__ __forceinline__ void load(const NF4View &w, int n0, int k0) {
-    const int tg = threadIdx.x & 255, grp = threadIdx.x >> 8;
+    const int tg = thread_in_group(), grp = wave_group();
     const int n = min(n0 + 128 * grp + (tg >> 1), w.N - 1);
     const int64_t blk = (static_cast<int64_t>(n) * w.K + k0) >> 6;
     p = *reinterpret_cast<const uint4 *>(w.packed + (blk << 5) + (tg & 1) * 16);
@@ -225,7 +243,7 @@ struct FwdPack {
     c2 = w.c2[blk >> 8];
   }
   __device__ __forceinline__ void expand(uint8_t *ws, const float2 *lut2, const float *t8, float mean) const {
-    const int tg = threadIdx.x & 255, grp = threadIdx.x >> 8;
+    const int tg = thread_in_group(), grp = wave_group();
     const int row = 128 * grp + (tg >> 1), half = tg & 1;
     const float chat = decode_absmax(t8[code], c2, mean);
     const uint32_t words[4] = {p.x, p.y, p.z, p.w};
@@ -256,7 +274,7 @@ struct DxPack {
   uint32_t code0, code1;
   float c20, c21;
   __device__ __forceinline__ void load(const NF4View &w, int n0, int k0) {
-    const int tg = threadIdx.x & 255, grp = threadIdx.x >> 8;
+    const int tg = thread_in_group(), grp = wave_group();
     const int n = n0 + 2 * (tg & 31);
     const int na = min(n, w.N - 1), nb = min(n + 1, w.N - 1);
     const int k = min(k0 + 128 * grp + 16 * (tg >> 5), w.K - 16);
@@ -272,7 +290,7 @@ struct DxPack {
   // only if the weight rows are zero too (dY past N is never loaded as data).
   __device__ __forceinline__ void expand(uint8_t *ws, const float2 *lut2, const float *t8, float mean, int n0,
                                          int N) const {
-    const int tg = threadIdx.x & 255, grp = threadIdx.x >> 8;
+    const int tg = thread_in_group(), grp = wave_group();
     const int np = tg & 31;
     const int kl = 128 * grp + 16 * (tg >> 5);
     const float ch0 = (n0 + 2 * np < N) ? decode_absmax(t8[code0], c20, mean) : 0.f;
@@ -342,7 +360,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   tile_coords((ncols + kBN - 1) / kBN, tr, tc);
   const int m0 = tr * kBM, c0 = tc * kBN;
   // wave-uniform group index in an SGPR, so the group branches are scalar
-  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const int grp = __builtin_amdgcn_readfirstlane(wave_group());
   const float mean = w.mean[0];
   const int KT = (Kc + kBK - 1) / kBK;
 
@@ -362,7 +380,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   // In a contraction tail (dX with N % 64 != 0) the DMA cannot zero the dY
   // columns past N; their chunks are clamped to valid data and the weight rows
   // past N are expanded as exact zeros, so they contribute nothing.
-  const int gw = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
+  const int gw = __builtin_amdgcn_readfirstlane(wave_in_group());
 
   f32x16_t acc[4][2];
   zero_acc(acc);
@@ -387,37 +405,55 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   // Refill loads always go out (clamped to the last step) to keep the register
   // flow branch-free; the extra loads near the end are never used.
   constexpr int kEndWait = kDx ? kWaitVm6Lgkm0 : kWaitVm3Lgkm0;
-  auto step0 = [&](auto cur_tag, int kt, P &pk) {
+  // `more` (a next step exists) is a compile-time flag: the unrolled loop body
+  // is branch-free, so the compiler's load-wait bookkeeping stays exact and it
+  // never drains the prefetches it does not need.
+  auto step0 = [&](auto cur_tag, auto more_tag, int kt, P &pk) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_tag)::value;
+    constexpr bool kMore = decltype(more_tag)::value;
     mfma_step(CUR ? sX1 : sX0, CUR ? sW1 : sW0, acc);
     raw_barrier<kWaitLgkm0>();
-    if (kt + 1 < KT) {
-      pack_expand(pk, CUR ? sW0 : sW1, kt + 1);
+    if constexpr (kMore) {
+      pack_expand(pk, CUR ? sW0 : sW1, min(kt + 1, KT - 1));
       pack_load(pk, min(kt + 3, KT - 1));
     }
     raw_barrier<kEndWait>();
   };
-  auto step1 = [&](auto cur_tag, int kt, P &pk) {
+  auto step1 = [&](auto cur_tag, auto more_tag, int kt, P &pk) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_tag)::value;
-    if (kt + 1 < KT) {
-      pack_expand(pk, CUR ? sW0 : sW1, kt + 1);
-      dma_left(CUR ? sX0 : sX1, L, ldl, m0, M, (kt + 1) * kBK, Kc, gw);
+    constexpr bool kMore = decltype(more_tag)::value;
+    if constexpr (kMore) {
+      pack_expand(pk, CUR ? sW0 : sW1, min(kt + 1, KT - 1));
+      dma_left(CUR ? sX0 : sX1, L, ldl, m0, M, min(kt + 1, KT - 1) * kBK, Kc, gw);
+      // The end-of-step wait counts on the refill loads being the newest
+      // memory operations of this wave: nothing may move across this point.
+      __builtin_amdgcn_sched_barrier(0);
       pack_load(pk, min(kt + 3, KT - 1));
     }
     raw_barrier<kWaitLgkm0>();
     mfma_step(CUR ? sX1 : sX0, CUR ? sW1 : sW0, acc);
     raw_barrier<kEndWait>();   // this group's DMA has landed
   };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // Every step of the loop prepares a next one (the step past the end expands
+  // and loads a clamped, never-used tile), so the loop body has no branches.
+  // An odd number of steps ends with one single step.
+  const int KT2 = KT & ~1;
   if (grp == 0) {
-    for (int kt = 0; kt < KT; kt += 2) {
-      step0(std::integral_constant<int, 0>(), kt, pk1);
-      if (kt + 1 < KT) step0(std::integral_constant<int, 1>(), kt + 1, pk0);
+    for (int kt = 0; kt < KT2; kt += 2) {
+      step0(C0(), T_(), kt, pk1);
+      step0(C1(), T_(), kt + 1, pk0);
     }
+    if (KT & 1) step0(C0(), F_(), KT - 1, pk1);
   } else {
-    for (int kt = 0; kt < KT; kt += 2) {
-      step1(std::integral_constant<int, 0>(), kt, pk1);
-      if (kt + 1 < KT) step1(std::integral_constant<int, 1>(), kt + 1, pk0);
+    for (int kt = 0; kt < KT2; kt += 2) {
+      step1(C0(), T_(), kt, pk1);
+      step1(C1(), T_(), kt + 1, pk0);
     }
+    if (KT & 1) step1(C0(), F_(), KT - 1, pk1);
   }
 
   // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A^T.
@@ -432,9 +468,9 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
     __syncthreads();
   }
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   uint8_t *region = (wave < 2 ? sX0 : wave < 4 ? sX1 : wave < 6 ? sW0 : sW1) + (wave & 1) * 16384;
-  store_tile(acc, region, out, ncols, m0 + (wave >> 2) * 128, c0 + (wave & 3) * 64, M, ncols);
+  store_tile(acc, region, out, ncols, m0 + wave_group() * 128, c0 + wave_in_group() * 64, M, ncols);
 }
 
 // ---------------------------------------------------------------------------
