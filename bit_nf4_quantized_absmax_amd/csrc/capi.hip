@@ -52,8 +52,13 @@ int from_hip(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; 
 
 size_t bf16_bytes(int64_t n) { return round_up(static_cast<size_t>(n) * 2, 256); }
 
-// Workspace of the forward pass: T [M, r] when the caller passes no T_out.
-size_t fwd_ws(int64_t M, int32_t r) { return bf16_bytes(M * r); }
+// Workspace of the forward pass.  M <= small_m_max(): the fp32 partials of
+// the down-projection (always needed).  Larger M: T [M, r] when the caller
+// passes no T_out.
+size_t fwd_ws(int64_t M, int64_t K, int32_t r) {
+  if (small_m_ok(M, r)) return small_m_ws_bytes(static_cast<int>(M), static_cast<int>(K), r);
+  return bf16_bytes(M * r);
+}
 
 // Workspace of the backward pass: T (recompute) | G | dA partials | dB partials.
 struct BwdWs {
@@ -119,7 +124,7 @@ int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *st
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd) {
   if (M < 0 || N < 1 || K < 64 || K % 64 || N % 8 || r < 1 || r > 128) return 0;
   if (M > 0 && M > kMaxElems / std::max(N, K)) return 0;
-  return is_bwd ? bwd_ws(M, N, K, r).total : fwd_ws(M, r);
+  return is_bwd ? bwd_ws(M, N, K, r).total : fwd_ws(M, K, r);
 }
 
 int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r, float scale,
@@ -202,9 +207,26 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
   int st = check_linear_shape(M, W, r, scale);
   if (st) return st;
   if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B) || !bf16_ok(Y) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
+  if (small_m_ok(M, r)) {
+    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->cols, r)) return QLORA_ERR_WORKSPACE;
+    SmGroup grp{};
+    grp.n = 1;
+    grp.M = static_cast<int>(M);
+    SmLinear &L = grp.lin[0];
+    L.X = X;
+    L.w = view_of(W);
+    L.A = A;
+    L.B = B;
+    L.P = static_cast<float *>(ws);
+    L.Y = Y;
+    L.Tout = T_out;
+    L.r = r;
+    L.scale = scale;
+    return from_hip(launch_small_m(grp, static_cast<hipStream_t>(stream)));
+  }
   uint16_t *T = T_out;
   if (!T) {
-    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, r)) return QLORA_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->cols, r)) return QLORA_ERR_WORKSPACE;
     T = static_cast<uint16_t *>(ws);
   }
   if (M == 0) return QLORA_OK;

@@ -31,6 +31,43 @@ struct NF4View {
 // Y [M, N] = X deq(W)^T + T B^T
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s);
+// ---- small-M forward (M <= small_m_max()) -------------------------------------
+// One linear of a group: Y = X deq(W)^T + T B^T.  T comes from Tin (bf16,
+// already scaled) or, when P is set, is formed as bf16(scale * sum of the
+// down-projection partials written to P by the first of the two launches).
+// Tout (nullable) receives that T.
+struct SmLinear {
+  const uint16_t *X;
+  NF4View w;
+  const uint16_t *A;
+  const uint16_t *B;
+  const uint16_t *Tin;
+  float *P;
+  uint16_t *Y;
+  uint16_t *Tout;
+  int r;
+  float scale;
+  int S;        // set by launch_small_m: column chunks of the down-projection
+  int kw;       // set by launch_small_m: columns per wave of the down-projection
+  int jtiles;   // set by launch_small_m
+};
+constexpr int kSmMaxGroup = 8;
+struct SmGroup {
+  SmLinear lin[kSmMaxGroup];
+  int down_start[kSmMaxGroup + 1];
+  int main_start[kSmMaxGroup + 1];
+  int n;
+  int M;
+};
+int small_m_max();
+// Whether the small-M kernels take this case (M <= small_m_max(), r % 8 == 0).
+bool small_m_ok(int64_t M, int r);
+// fp32 partial buffer P of one linear: [S <= 2][M][r].
+size_t small_m_ws_bytes(int M, int K, int r);
+hipError_t launch_small_m(SmGroup &grp, hipStream_t s);
+// Small-M form of launch_matmul_fwd with T given (requires small_m_ok).
+hipError_t launch_small_m_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T, const uint16_t *B,
+                              int r, uint16_t *Y, hipStream_t s);
 // dX [M, K] = dY deq(W) + G A
 hipError_t launch_matmul_dx(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
                             const uint16_t *A, int r, uint16_t *dX, hipStream_t s);

@@ -476,6 +476,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
 // ---------------------------------------------------------------------------
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s) {
+  if (small_m_ok(M, r)) return launch_small_m_fwd(X, M, w, T, B, r, Y, s);
   const int tiles = ((M + kBM - 1) / kBM) * ((w.N + kBN - 1) / kBN);
   hipLaunchKernelGGL(k_matmul<false>, dim3(tiles), dim3(kThreadsMM), 0, s, X, M, w, T, B, r, Y);
   return hipGetLastError();

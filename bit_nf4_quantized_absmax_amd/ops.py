@@ -116,15 +116,23 @@ def _lin_checks(X, w, A, B, r_expect=None):
     return X.shape[0], N, K, r
 
 
-def linear_fwd(X, w, A, B, scale, T_out=None):
+def linear_fwd(X, w, A, B, scale, T_out=None, out=None, workspace=None):
     """Y = X deq(W)^T + scale (X A^T) B^T; returns (Y, T) with T = scale X A^T [M, r]."""
     M, N, K, r = _lin_checks(X, w, A, B)
-    Y = torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", (M, N))
     T = T_out if T_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
     _need(T, torch.bfloat16, "T", (M, r))
+    ws_bytes = lib().qlora_linear_workspace_bytes(M, N, K, r, 0)
+    ws = None
+    if ws_bytes:
+        ws = workspace if workspace is not None else torch.empty(ws_bytes, dtype=torch.uint8, device=X.device)
+        if ws.numel() * ws.element_size() < ws_bytes:
+            raise ValueError("workspace smaller than %d bytes" % ws_bytes)
     st = w.struct()
     check(lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(Y),
-                                 _ptr(T), None, 0, _stream(X)), "qlora_linear_fwd")
+                                 _ptr(T), None if ws is None else _ptr(ws), ws_bytes, _stream(X)),
+          "qlora_linear_fwd")
     return Y, T
 
 

@@ -105,7 +105,10 @@ int qlora_quantize_nf4(const float *W, const qlora_nf4_weight *out, void *ws,
 int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *stream);
 
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
- * (is_bwd = 1) at these sizes.  0 if the shape is unsupported. */
+ * (is_bwd = 1) at these sizes.  0 if the shape is unsupported, and 0 for a
+ * forward pass at M = 0.  A forward pass at 1 <= M <= 64 with r % 8 == 0
+ * (the decode regime) always needs its workspace: it holds fp32 partial sums
+ * of X A^T, at most 2 x M x r floats. */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd);
 
 /* Forward: Y [M, N] = X [M, K] deq(W)^T + scale (X A^T) B^T.
@@ -113,6 +116,14 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
  *   T_out [M, r] (nullable): receives T = scale X A^T in bf16 (the LoRA
  *   intermediate with the scale applied once in fp32 before rounding) for
  *   reuse in the backward pass; when NULL, T lives in the workspace.
+ *   ws: device memory of qlora_linear_workspace_bytes(M, N, K, r, 0) bytes,
+ *   16-byte aligned; it may be NULL only when that size is 0.
+ *   At 1 <= M <= 64 with r % 8 == 0 the pass takes a decode-regime route: two
+ *   launches, the second streaming the packed weight once with all of its
+ *   loads in flight (bandwidth-bound), which applies each block constant to
+ *   the bf16 level product in fp32 (bf16(NF4[q]) * c_hat) instead of rounding
+ *   NF4[q] * c_hat to bf16 (within the same tolerance); otherwise two MFMA tile
+ *   kernels that dequantize exactly as qlora_dequantize_nf4 does.
  * Requires K % 64 == 0 (blocks never straddle rows), 1 <= r <= 128, M >= 0
  * (M = 0 launches nothing), N >= 1.  Pages: automatone.win, "QLoRA paper
  * explained", How it works; creativeworksofknowledge.com, "QLoRA: Fine-Tune

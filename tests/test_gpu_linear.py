@@ -130,6 +130,42 @@ def test_small_m_llama7b(M, li):
     assert_close(as_f64(Y), Yr, "small-M Y")
 
 
+@pytest.mark.parametrize("M,N,K,r", [
+    (1, 776, 576, 8),       # odd number of 64-blocks per row, N not a multiple of 16
+    (3, 512, 320, 16),
+    (17, 264, 1024, 24),    # two 16-token tiles
+    (33, 128, 4160, 64),    # three token tiles, K past one load batch
+    (48, 136, 704, 128),
+    (64, 512, 13056, 64),   # four token tiles, several load batches
+    (8, 256, 512, 100),     # r % 8 != 0 takes the general path
+])
+def test_small_m_shapes(M, N, K, r):
+    print("small-M shape", (M, N, K, r), flush=True)
+    W, X, A, B, _ = _inputs(M, N, K, r, 900 + M)
+    w = q.NF4Weight.quantize(to_dev_f32(W))
+    Xd, Ad, Bd = to_dev_bf16(X), to_dev_bf16(A), to_dev_bf16(B)
+    s = 16.0 / r
+    Y, T = q.linear_fwd(Xd, w, Ad, Bd, s)
+    T2 = q.lora_down(Xd, Ad, s)
+    Y2 = q.nf4_matmul_fwd(Xd, w, T2, Bd)
+    torch.cuda.synchronize()
+    Yr, Tr = olin.linear_fwd(X, _oracle_wt(W), A, B, s)
+    assert_close(as_f64(Y), Yr, "small-M Y")
+    assert_close(as_f64(T), np.float32(s) * Tr, "small-M T")
+    assert_close(as_f64(Y2), Yr, "small-M Y (T given)")
+
+
+def test_small_m_deterministic():
+    W, X, A, B, _ = _inputs(16, 1024, 4096, 64, 950)
+    w = q.NF4Weight.quantize(to_dev_f32(W))
+    Xd, Ad, Bd = to_dev_bf16(X), to_dev_bf16(A), to_dev_bf16(B)
+    a = q.linear_fwd(Xd, w, Ad, Bd, 0.25)
+    b = q.linear_fwd(Xd, w, Ad, Bd, 0.25)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 def test_llama7b_full_size_sampled():
     """Full 7B shapes at 8192 tokens in the benchmark's launch configuration;
     the oracle checks sampled rows / columns spanning every tile row."""
