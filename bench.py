@@ -17,10 +17,11 @@ Also reported on the same JSON line:
                 events around each of its launches inside the timed region
   cpu_baseline  the CPU oracle on a bounded token sample of the same step
   small_m       forward-only M = 1 / 16 / 64 over 4 weight sets (> the 256 MB
-                Infinity Cache), algorithmic HBM GB/s
+                Infinity Cache), replayed from a HIP graph, algorithmic HBM GB/s
   quantize      quantize throughput on the 7 weights (algorithmic GB/s)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+                       [--copy-probe-mib MiB]
 """
 
 import argparse
@@ -47,7 +48,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="skip small-M and quantize figures")
-    p.add_argument("--cpu-tokens", type=int, default=256, help="token sample for the CPU oracle")
+    p.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device-to-device copy of this many MiB first (a reference "
+                        "dispatch for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -58,6 +62,34 @@ def linear_flops(M, N, K, r):
 def small_m_bytes(M, N, K, r):
     # packed codes + 8-bit constants + fp32 group scales + mean + X + Y + A + B
     return N * K / 2 + N * K / 64 + 4 * N * K / 16384 + 4 + 2 * M * K + 2 * M * N + 2 * r * K + 2 * r * N
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "matmul_llama7b_m8192_hbm_traffic.md")
+MATMUL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_absmax_amd", "csrc", f) for f in ("matmul.hip", "common.h")]
+
+
+def matmul_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in MATMUL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
+    when there is none or the matmul sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("source_sha256") != matmul_source_sha256():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("traffic_bytes_per_launch")
 
 
 def log(*a):
@@ -134,7 +166,12 @@ def cpu_baseline(cfg, tokens):
 
 
 def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
-    """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache)."""
+    """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache).
+
+    The 7 linear_fwd calls of each weight set are captured once in a HIP graph
+    (the library makes no allocation and no memset inside a call); the timed
+    region replays the graphs.  GB/s = algorithmic bytes of the 7 linears /
+    time per layer."""
     r = cfg.rank
     sets = []
     for s in range(4):
@@ -155,27 +192,38 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
             B = workloads.device_normal((N, r), workloads.LORA_STD, 93000 + li, dev, torch.bfloat16)
             Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
             T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
-            lin_in.append((X, A, B, Y, T))
+            nws = max(q.lib().qlora_linear_workspace_bytes(M, N, K, r, 0), 16)
+            wsp = torch.empty(nws, dtype=torch.uint8, device=dev)
+            lin_in.append((X, A, B, Y, T, wsp))
         nbytes = sum(small_m_bytes(M, l.out_features, l.in_features, r) for l in cfg.linears)
 
         def one_layer(ws):
-            for (X, A, B, Y, T), w in zip(lin_in, ws):
-                q.linear_fwd(X, w, A, B, cfg.scale, T_out=T)
+            for (X, A, B, Y, T, wsp), w in zip(lin_in, ws):
+                q.linear_fwd(X, w, A, B, cfg.scale, T_out=T, out=Y, workspace=wsp)
 
         for ws in sets:
             one_layer(ws)
         torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for ws in sets:
+                one_layer(ws)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            for ws in sets:
-                one_layer(ws)
+            graph.replay()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
         gbs = nbytes / (us * 1e-6) / 1e9
-        out["M%d" % M] = dict(us_per_layer=round(us, 2), bytes_per_layer=int(nbytes), GBps=round(gbs, 1),
+        out["M%d" % M] = dict(us_per_layer=round(us, 2), launches_per_layer=2 * len(cfg.linears),
+                              bytes_per_layer=int(nbytes), GBps=round(gbs, 1),
                               frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        del graph
     del sets
     torch.cuda.empty_cache()
     return out
@@ -218,6 +266,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 18                 # float32 elements
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
     cfg = workloads.CONFIGS[1]
     scale = cfg.scale
     log("building inputs for", cfg.name)
@@ -253,9 +310,11 @@ def main():
     dom_key = max(kern, key=lambda k: kern[k]["total_ms"])
     dom = kern[dom_key]
     achieved = dom["flops_per_launch"] / (dom["avg_us"] * 1e-6) / 1e12
+    dom_kernel = "qlora::k_matmul<false>" if dom_key == "fwd" else "qlora::k_matmul<true>"
     roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
-                    kernel="k_matmul_fwd" if dom_key == "fwd" else "k_matmul_dx",
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=recorded_traffic(dom_kernel),
+                    traffic_unit="HBM bytes per launch (PMC FETCH_SIZE/WRITE_SIZE, copy-scaled)",
+                    kernel=dom_kernel + (" (forward)" if dom_key == "fwd" else " (dX)"),
                     avg_launch_us=round(dom["avg_us"], 2),
                     flops_per_launch=dom["flops_per_launch"])
     other = {k: dict(avg_us=round(v["avg_us"], 2), TFLOPs=round(v["flops_per_launch"] / (v["avg_us"] * 1e-6) / 1e12, 1),
