@@ -17,7 +17,8 @@ Also reported on the same JSON line:
                 events around each of its launches inside the timed region
   cpu_baseline  the CPU oracle on a bounded token sample of the same step
   small_m       forward-only M = 1 / 16 / 64 over 4 weight sets (> the 256 MB
-                Infinity Cache), replayed from a HIP graph, algorithmic HBM GB/s
+                Infinity Cache), replayed from HIP graphs, algorithmic HBM GB/s:
+                7 single-linear calls per layer and one grouped call
   quantize      quantize throughput on the 7 weights (algorithmic GB/s)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
@@ -168,10 +169,13 @@ def cpu_baseline(cfg, tokens):
 def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
     """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache).
 
-    The 7 linear_fwd calls of each weight set are captured once in a HIP graph
-    (the library makes no allocation and no memset inside a call); the timed
-    region replays the graphs.  GB/s = algorithmic bytes of the 7 linears /
-    time per layer."""
+    Two launch patterns, each captured once in a HIP graph and replayed (the
+    library makes no allocation and no memset inside a call):
+      per_linear  7 linear_fwd calls per layer (2 launches each)
+      grouped     one linear_fwd_group call over the 7 linears (2 launches)
+    GB/s = algorithmic bytes of the 7 linears / time per layer."""
+    import ctypes
+    from bit_nf4_quantized_absmax_amd._capi import LinearDescStruct
     r = cfg.rank
     sets = []
     for s in range(4):
@@ -196,34 +200,49 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
             wsp = torch.empty(nws, dtype=torch.uint8, device=dev)
             lin_in.append((X, A, B, Y, T, wsp))
         nbytes = sum(small_m_bytes(M, l.out_features, l.in_features, r) for l in cfg.linears)
+        group_items = [[(X, w, A, B, cfg.scale, T, Y) for (X, A, B, Y, T, _), w in zip(lin_in, ws)] for ws in sets]
+        structs = [[w.struct() for w in ws] for ws in sets]
+        descs = [(LinearDescStruct * len(cfg.linears))(*[
+            LinearDescStruct(X.data_ptr(), ctypes.pointer(st), A.data_ptr(), B.data_ptr(), r, cfg.scale,
+                             Y.data_ptr(), T.data_ptr()) for (X, A, B, Y, T, _), st in zip(lin_in, sts)])
+            for sts in structs]
+        gws_bytes = max(q.lib().qlora_linear_group_workspace_bytes(len(cfg.linears), d, M) for d in descs)
+        gws = torch.empty(max(gws_bytes, 16), dtype=torch.uint8, device=dev)
 
-        def one_layer(ws):
+        def per_linear(ws):
             for (X, A, B, Y, T, wsp), w in zip(lin_in, ws):
                 q.linear_fwd(X, w, A, B, cfg.scale, T_out=T, out=Y, workspace=wsp)
 
-        for ws in sets:
-            one_layer(ws)
-        torch.cuda.synchronize()
-        stream = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for ws in sets:
-                one_layer(ws)
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
-        gbs = nbytes / (us * 1e-6) / 1e9
-        out["M%d" % M] = dict(us_per_layer=round(us, 2), launches_per_layer=2 * len(cfg.linears),
-                              bytes_per_layer=int(nbytes), GBps=round(gbs, 1),
-                              frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
-        del graph
+        def grouped(si):
+            q.linear_fwd_group(group_items[si], workspace=gws)
+
+        res = {}
+        for name, fn in (("per_linear", lambda si: per_linear(sets[si])), ("grouped", grouped)):
+            for si in range(len(sets)):
+                fn(si)
+            torch.cuda.synchronize()
+            stream = torch.cuda.Stream()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for si in range(len(sets)):
+                    fn(si)
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+            gbs = nbytes / (us * 1e-6) / 1e9
+            res[name] = dict(us_per_layer=round(us, 2), GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+            del graph
+        res["per_linear"]["launches_per_layer"] = 2 * len(cfg.linears)
+        res["grouped"]["launches_per_layer"] = 2
+        res["bytes_per_layer"] = int(nbytes)
+        out["M%d" % M] = res
     del sets
     torch.cuda.empty_cache()
     return out

@@ -7,11 +7,11 @@ package only marshals torch tensors to it.
 """
 
 from ._capi import EXPORTED, LIB_PATH, QLoRAError, lib, status_string  # noqa: F401
-from .ops import (NF4Weight, QLoRALinear, QLoRALinearFn, linear_bwd, linear_fwd, lora_down,  # noqa: F401
-                  lora_grad_in, lora_grads, nf4_matmul_dx, nf4_matmul_fwd, nf4_sizes)
+from .ops import (NF4Weight, QLoRALinear, QLoRALinearFn, linear_bwd, linear_fwd, linear_fwd_group,  # noqa: F401
+                  lora_down, lora_grad_in, lora_grads, nf4_matmul_dx, nf4_matmul_fwd, nf4_sizes)
 
 __all__ = [
-    "NF4Weight", "QLoRALinear", "QLoRALinearFn", "linear_fwd", "linear_bwd", "lora_down",
+    "NF4Weight", "QLoRALinear", "QLoRALinearFn", "linear_fwd", "linear_fwd_group", "linear_bwd", "lora_down",
     "nf4_matmul_fwd", "lora_grad_in", "nf4_matmul_dx", "lora_grads", "nf4_sizes", "lib",
     "QLoRAError", "status_string",
 ]

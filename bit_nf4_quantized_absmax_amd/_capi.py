@@ -22,6 +22,7 @@ EXPORTED = (
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in", "qlora_nf4_matmul_dx",
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
+    "qlora_linear_group_workspace_bytes", "qlora_linear_fwd_group",
 )
 
 
@@ -39,6 +40,19 @@ class NF4WeightStruct(ctypes.Structure):
         ("mean", ctypes.c_void_p),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+    ]
+
+
+class LinearDescStruct(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p),
+        ("W", ctypes.POINTER(NF4WeightStruct)),
+        ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("r", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("Y", ctypes.c_void_p),
+        ("T_out", ctypes.c_void_p),
     ]
 
 
@@ -64,6 +78,8 @@ _SIGS = {
     "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
     "qlora_lora_grads_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_group_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(LinearDescStruct), _i64]),
+    "qlora_linear_fwd_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearDescStruct), _i64, _vp, _sz, _vp]),
 }
 
 

@@ -238,6 +238,66 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
   return from_hip(launch_matmul_fwd(X, m, v, T, B, r, Y, s));
 }
 
+static bool group_small_m(int count, const qlora_linear_desc *d, int64_t M) {
+  for (int i = 0; i < count; ++i)
+    if (!small_m_ok(M, d[i].r)) return false;
+  return true;
+}
+
+size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *d, int64_t M) {
+  if (count < 1 || count > kSmMaxGroup || !d) return 0;
+  size_t total = 0, most = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!d[i].W || check_linear_shape(M, d[i].W, d[i].r, d[i].scale)) return 0;
+    const size_t b = fwd_ws(M, d[i].W->cols, d[i].r);
+    total += b;
+    most = std::max(most, b);
+  }
+  return group_small_m(count, d, M) ? total : most;
+}
+
+int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (count < 1 || count > kSmMaxGroup || !d) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    if (!d[i].W) return QLORA_ERR_INVALID_ARG;
+    int st = check_linear_shape(M, d[i].W, d[i].r, d[i].scale);
+    if (st) return st;
+    if (!bf16_ok(d[i].X) || !bf16_ok(d[i].A) || !bf16_ok(d[i].B) || !bf16_ok(d[i].Y) || !bf16_opt(d[i].T_out))
+      return QLORA_ERR_INVALID_ARG;
+  }
+  const size_t need = qlora_linear_group_workspace_bytes(count, d, M);
+  if (need && (!ws || !aligned(ws, 16) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (group_small_m(count, d, M)) {
+    SmGroup grp{};
+    grp.n = count;
+    grp.M = static_cast<int>(M);
+    char *p = static_cast<char *>(ws);
+    for (int i = 0; i < count; ++i) {
+      SmLinear &L = grp.lin[i];
+      L.X = d[i].X;
+      L.w = view_of(d[i].W);
+      L.A = d[i].A;
+      L.B = d[i].B;
+      L.P = reinterpret_cast<float *>(p);
+      L.Y = d[i].Y;
+      L.Tout = d[i].T_out;
+      L.r = d[i].r;
+      L.scale = d[i].scale;
+      p += fwd_ws(M, d[i].W->cols, d[i].r);
+    }
+    return from_hip(launch_small_m(grp, s));
+  }
+  for (int i = 0; i < count; ++i) {
+    int st = qlora_linear_fwd(d[i].X, M, d[i].W, d[i].A, d[i].B, d[i].r, d[i].scale, d[i].Y, d[i].T_out, ws,
+                              ws_bytes, stream);
+    if (st) return st;
+  }
+  return QLORA_OK;
+}
+
 int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,
                      const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
                      uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {

@@ -56,15 +56,35 @@ struct SmGroup {
   SmLinear lin[kSmMaxGroup];
   int down_start[kSmMaxGroup + 1];
   int main_start[kSmMaxGroup + 1];
+  // Work plan of the GEMV kernel (set by launch_small_m_gemv): first item
+  // (row tile) and first chunk index (2048 columns of a tile) of each linear,
+  // chunks per tile.
+  int item0[kSmMaxGroup + 1];
+  int cost0[kSmMaxGroup + 1];
+  int nch[kSmMaxGroup];
+  int xoff[kSmMaxGroup];   // byte offset of each linear's X in the GEMV kernel's LDS copy
+  int toff[kSmMaxGroup];   // byte offset of each linear's T there
+  int xs0[kSmMaxGroup + 1];   // first X copy slot (64 x 16 bytes) of each linear
+  int dg0[kSmMaxGroup + 1];   // first (adapter row, chunk) item of each linear in k_sm_down_gemv
   int n;
   int M;
 };
 int small_m_max();
 // Whether the small-M kernels take this case (M <= small_m_max(), r % 8 == 0).
 bool small_m_ok(int64_t M, int r);
-// fp32 partial buffer P of one linear: [S <= 2][M][r].
+// fp32 partial buffer P of one linear: [S <= 4][M][r].
 size_t small_m_ws_bytes(int M, int K, int r);
 hipError_t launch_small_m(SmGroup &grp, hipStream_t s);
+// Dequant-GEMV for M <= small_m_gemv_max() (S and the partials already
+// prepared by launch_small_m).
+int small_m_gemv_max();
+// Whether the group takes the one-token path with X in LDS; if so the
+// down-projection partials come from launch_small_m_down_gemv, one slice per
+// 2048 columns (S = ceil(K / 2048)).
+bool small_m_gemv_xl(const SmGroup &grp);
+int small_m_gemv_slices(int K);
+hipError_t launch_small_m_down_gemv(SmGroup &grp, hipStream_t s);
+hipError_t launch_small_m_gemv(SmGroup &grp, hipStream_t s);
 // Small-M form of launch_matmul_fwd with T given (requires small_m_ok).
 hipError_t launch_small_m_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T, const uint16_t *B,
                               int r, uint16_t *Y, hipStream_t s);

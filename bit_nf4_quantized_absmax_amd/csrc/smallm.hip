@@ -8,7 +8,7 @@
 // every load a wave needs before the first use.
 //
 // k_sm_down: partial LoRA down-projections P[s] = X[:, chunk s] A[:, chunk s]^T
-//   (fp32, unscaled; at most 2 column chunks), one workgroup per (chunk, 16
+//   (fp32, unscaled; at most 4 column chunks), one workgroup per (chunk, 16
 //   adapter rows); the 16 waves split the chunk and are summed in LDS in wave
 //   order.
 // k_sm_main: one workgroup per 16 weight rows x the whole K.  Wave w takes the
@@ -22,6 +22,8 @@
 //   rounding of the sums, within the matmul tolerance.  Waves 0 .. 3 add
 //   T B^T, T = bf16(s * sum of the partials) (or T as given).  The 16 wave
 //   accumulators are summed in LDS in wave order: results are deterministic.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -347,11 +349,14 @@ __global__ __launch_bounds__(kSmThreads) void k_sm_main(SmGroup grp) {
 }
 
 // ---------------------------------------------------------------------------
-// Column split of the down-projection: at most kSmMaxSplits partial slices;
-// kw columns per wave, a multiple of 32.
+// Column split of the down-projection into partial slices; kw columns per
+// wave, a multiple of 32.
 static int sm_splits(int M, int K, int *kw_out) {
-  (void)M;
-  const int per = kSmWaves * 32 * kSmMaxSplits;
+  // GEMV regime: up to 4 slices, aiming at 256 columns per wave (one load
+  // batch).  Wider token tiles: at most 2 slices (their registers hold them).
+  const int target = M <= small_m_gemv_max() ? std::min(4, (K + kSmWaves * 256 - 1) / (kSmWaves * 256))
+                                             : kSmMaxSplits;
+  const int per = kSmWaves * 32 * target;
   const int kw = 32 * ((K + per - 1) / per);
   if (kw_out) *kw_out = kw;
   return (K + kSmWaves * kw - 1) / (kSmWaves * kw);
@@ -360,7 +365,8 @@ static int sm_splits(int M, int K, int *kw_out) {
 bool small_m_ok(int64_t M, int r) { return M >= 1 && M <= kSmMaxM && r % 8 == 0; }
 
 size_t small_m_ws_bytes(int M, int K, int r) {
-  const int S = sm_splits(M, K, nullptr);
+  int S = sm_splits(M, K, nullptr);
+  if (M == 1) S = std::max(S, small_m_gemv_slices(K));
   return (static_cast<size_t>(S) * M * r * sizeof(float) + 255) / 256 * 256;
 }
 
@@ -373,6 +379,19 @@ static void sm_launch_main(bool p, int grid, const SmGroup &grp, hipStream_t s) 
 }
 
 hipError_t launch_small_m(SmGroup &grp, hipStream_t s) {
+  if (grp.M <= small_m_gemv_max() && small_m_gemv_xl(grp)) {
+    bool any_p = false;
+    for (int i = 0; i < grp.n; ++i) {
+      SmLinear &L = grp.lin[i];
+      L.S = small_m_gemv_slices(L.w.K);
+      any_p = any_p || L.P != nullptr;
+    }
+    if (any_p) {
+      hipError_t e = launch_small_m_down_gemv(grp, s);
+      if (e != hipSuccess) return e;
+    }
+    return launch_small_m_gemv(grp, s);
+  }
   int down = 0, main = 0;
   bool any_down = false;
   for (int i = 0; i < grp.n; ++i) {
@@ -400,6 +419,7 @@ hipError_t launch_small_m(SmGroup &grp, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (grp.M <= small_m_gemv_max()) return launch_small_m_gemv(grp, s);
   const bool p = grp.lin[0].P != nullptr;       // all linears of a group alike
   switch (mb) {
     case 1: sm_launch_main<1>(p, main, grp, s); break;

@@ -136,6 +136,48 @@ def linear_fwd(X, w, A, B, scale, T_out=None, out=None, workspace=None):
     return Y, T
 
 
+def linear_fwd_group(linears, scale=None, workspace=None):
+    """Forward of up to 8 independent linears sharing the token count M.
+
+    `linears` is a sequence of (X, w, A, B, scale) or (X, w, A, B, scale, T_out,
+    Y_out) tuples; returns the list of (Y, T).  Same results as calling
+    linear_fwd on each; in the decode regime the group costs two launches."""
+    from ._capi import LinearDescStruct
+    if not 1 <= len(linears) <= 8:
+        raise ValueError("a group holds 1 to 8 linears")
+    M = None
+    outs, descs, structs = [], [], []
+    for item in linears:
+        X, w, A, B, sc = item[:5]
+        T_out = item[5] if len(item) > 5 else None
+        Y_out = item[6] if len(item) > 6 else None
+        m, N, K, r = _lin_checks(X, w, A, B)
+        if M is None:
+            M = m
+        elif m != M:
+            raise ValueError("all linears of a group share M")
+        Y = Y_out if Y_out is not None else torch.empty(m, N, dtype=torch.bfloat16, device=X.device)
+        _need(Y, torch.bfloat16, "Y", (m, N))
+        T = T_out if T_out is not None else torch.empty(m, r, dtype=torch.bfloat16, device=X.device)
+        _need(T, torch.bfloat16, "T", (m, r))
+        st = w.struct()
+        structs.append(st)
+        descs.append(LinearDescStruct(X.data_ptr(), ctypes.pointer(st), A.data_ptr(), B.data_ptr(), r, float(sc),
+                                      Y.data_ptr(), T.data_ptr()))
+        outs.append((Y, T))
+    arr = (LinearDescStruct * len(descs))(*descs)
+    ws_bytes = lib().qlora_linear_group_workspace_bytes(len(descs), arr, M)
+    ws = None
+    if ws_bytes:
+        ws = workspace if workspace is not None else torch.empty(ws_bytes, dtype=torch.uint8,
+                                                                  device=linears[0][0].device)
+        if ws.numel() * ws.element_size() < ws_bytes:
+            raise ValueError("workspace smaller than %d bytes" % ws_bytes)
+    check(lib().qlora_linear_fwd_group(len(descs), arr, M, None if ws is None else _ptr(ws), ws_bytes,
+                                       _stream(linears[0][0])), "qlora_linear_fwd_group")
+    return outs
+
+
 def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=True, workspace=None):
     """Returns (dX, dA, dB) (None where not requested); T = scale X A^T as
     returned by linear_fwd, or None (recomputed)."""

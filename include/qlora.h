@@ -108,7 +108,7 @@ int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *st
  * (is_bwd = 1) at these sizes.  0 if the shape is unsupported, and 0 for a
  * forward pass at M = 0.  A forward pass at 1 <= M <= 64 with r % 8 == 0
  * (the decode regime) always needs its workspace: it holds fp32 partial sums
- * of X A^T, at most 2 x M x r floats. */
+ * of X A^T, at most 4 x M x r floats. */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd);
 
 /* Forward: Y [M, N] = X [M, K] deq(W)^T + scale (X A^T) B^T.
@@ -131,6 +131,37 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
 int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
                      const uint16_t *A, const uint16_t *B, int32_t r, float scale,
                      uint16_t *Y, uint16_t *T_out, void *ws, size_t ws_bytes, void *stream);
+
+/* One linear of a grouped forward call (all pointers device memory, same
+ * layouts and rules as qlora_linear_fwd). */
+typedef struct {
+  const uint16_t *X;            /* [M, K] */
+  const qlora_nf4_weight *W;    /* N x K (host pointer to the descriptor) */
+  const uint16_t *A;            /* [r, K] */
+  const uint16_t *B;            /* [N, r] */
+  int32_t r;
+  float scale;
+  uint16_t *Y;                  /* [M, N] */
+  uint16_t *T_out;              /* [M, r], nullable */
+} qlora_linear_desc;
+
+/* Workspace bytes for qlora_linear_fwd_group (0 if any shape is unsupported,
+ * count < 1 or count > 8). */
+size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *descs, int64_t M);
+
+/* Forward of up to 8 independent linears that share the token count M, each
+ * exactly as qlora_linear_fwd computes it (same results, bit for bit).  In
+ * the decode regime (1 <= M <= 64, every r % 8 == 0) the whole group takes
+ * two launches: one for all the down-projection partials, one streaming all
+ * the packed weights, so that launch latency is paid once per group (for
+ * example the q, k, v projections of a layer, which share their input).
+ * Outside that regime the linears run one after another.  ws: device memory
+ * of qlora_linear_group_workspace_bytes bytes, 16-byte aligned.  Validation of
+ * every descriptor happens before any launch.  Pages: automatone.win,
+ * "QLoRA paper explained", How it works; creativeworksofknowledge.com,
+ * "QLoRA: Fine-Tune 70B on One GPU", Code (adapters on every linear). */
+int qlora_linear_fwd_group(int count, const qlora_linear_desc *descs, int64_t M, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /* Backward: given dY [M, N], X [M, K] and optionally T = scale X A^T [M, r]
  * as written by qlora_linear_fwd (NULL: recomputed), writes

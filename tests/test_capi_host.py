@@ -103,6 +103,20 @@ def test_validation_rejects_before_launch():
     assert L.qlora_lora_grad_in(P, 4, 60, P, 200, 1.0, P, None) == SHAPE
     assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 8, P, P, None, 0, None) == WS
     assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 0, P, P, P, 1 << 30, None) == SHAPE
+    # grouped forward: bad count, bad descriptor, workspace
+    D = _capi.LinearDescStruct
+    ok = D(0x20000, ctypes.pointer(w), 0x20000, 0x20000, 8, 1.0, 0x20000, 0)
+    arr = (D * 1)(ok)
+    assert L.qlora_linear_fwd_group(0, arr, 8, P, 1 << 20, None) == INVALID
+    assert L.qlora_linear_fwd_group(9, arr, 8, P, 1 << 20, None) == INVALID
+    assert L.qlora_linear_group_workspace_bytes(1, arr, 8) > 0
+    assert L.qlora_linear_group_workspace_bytes(0, arr, 8) == 0
+    assert L.qlora_linear_fwd_group(1, arr, 8, None, 0, None) == WS
+    badk = (D * 1)(D(0x20000, ctypes.pointer(wk), 0x20000, 0x20000, 8, 1.0, 0x20000, 0))
+    assert L.qlora_linear_fwd_group(1, badk, 8, P, 1 << 20, None) == SHAPE
+    nulx = (D * 1)(D(0, ctypes.pointer(w), 0x20000, 0x20000, 8, 1.0, 0x20000, 0))
+    assert L.qlora_linear_fwd_group(1, nulx, 8, P, 1 << 20, None) == INVALID
+    assert L.qlora_linear_fwd_group(1, arr, 0, None, 0, None) == OK
     # misaligned weight buffers
     mis = _capi.NF4WeightStruct(0x10008, 0x11000, 0x12000, 0x13000, 64, 64)
     assert L.qlora_dequantize_nf4(ctypes.byref(mis), P, None) == INVALID

@@ -166,6 +166,31 @@ def test_small_m_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("M", [1, 3, 16, 40, 100])
+def test_linear_fwd_group_matches_single_calls(M):
+    """A group of linears with different shapes: every output equals the
+    single-linear call bit for bit, and the oracle within tolerance."""
+    print("group case M", M, flush=True)
+    shapes = [(512, 1024, 64), (776, 576, 8), (264, 4160, 32), (1024, 512, 16)]
+    items, refs = [], []
+    for i, (N, K, r) in enumerate(shapes):
+        W, X, A, B, _ = _inputs(M, N, K, r, 1000 + 10 * i + M)
+        w = q.NF4Weight.quantize(to_dev_f32(W))
+        Xd, Ad, Bd = to_dev_bf16(X), to_dev_bf16(A), to_dev_bf16(B)
+        s = 16.0 / r
+        items.append((Xd, w, Ad, Bd, s))
+        refs.append((W, X, A, B, s))
+    outs = q.linear_fwd_group(items)
+    singles = [q.linear_fwd(*it) for it in items]
+    torch.cuda.synchronize()
+    for (Y, T), (Y1, T1), (W, X, A, B, s) in zip(outs, singles, refs):
+        assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))
+        assert torch.equal(T.view(torch.int16), T1.view(torch.int16))
+        Yr, Tr = olin.linear_fwd(X, _oracle_wt(W), A, B, s)
+        assert_close(as_f64(Y), Yr, "group Y")
+        assert_close(as_f64(T), np.float32(s) * Tr, "group T")
+
+
 def test_llama7b_full_size_sampled():
     """Full 7B shapes at 8192 tokens in the benchmark's launch configuration;
     the oracle checks sampled rows / columns spanning every tile row."""
