@@ -117,6 +117,8 @@ class Layer:
         self.dX = torch.empty(M, K, dtype=bf, device=dev)
         ws = q.lib().qlora_lora_grads_workspace_bytes(M, N, K, r)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        self.gws = torch.empty(max(q.lib().qlora_lora_grad_in_workspace_bytes(N, r), 16), dtype=torch.uint8,
+                               device=dev)
         self.flops = linear_flops(M, N, K, r)
         self.fwd_mm_flops = 2.0 * M * N * K + 2.0 * M * r * N
         self.dx_mm_flops = 2.0 * M * N * K + 2.0 * M * r * K
@@ -131,7 +133,7 @@ def run_step(q, torch, layers, scale, events=None):
         q.nf4_matmul_fwd(L.X, L.w, L.T, L.B, out=L.Y)
         if events is not None:
             events["fwd"][-1][1].record()
-        q.lora_grad_in(L.dY, L.B, scale, out=L.G)
+        q.lora_grad_in(L.dY, L.B, scale, out=L.G, workspace=L.gws)
         if events is not None:
             events["dx"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), L))
             events["dx"][-1][0].record()

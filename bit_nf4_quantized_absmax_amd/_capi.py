@@ -20,7 +20,8 @@ EXPORTED = (
     "qlora_status_string", "qlora_version", "qlora_nf4_sizes",
     "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_dequantize_nf4",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
-    "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in", "qlora_nf4_matmul_dx",
+    "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in_workspace_bytes", "qlora_lora_grad_in",
+    "qlora_nf4_matmul_dx",
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
     "qlora_linear_group_workspace_bytes", "qlora_linear_fwd_group",
 )
@@ -74,7 +75,8 @@ _SIGS = {
                                         _vp, _sz, _vp]),
     "qlora_lora_down": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp]),
     "qlora_nf4_matmul_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
-    "qlora_lora_grad_in": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp]),
+    "qlora_lora_grad_in_workspace_bytes": (_sz, [_i64, _i32]),
+    "qlora_lora_grad_in": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
     "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
     "qlora_lora_grads_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),

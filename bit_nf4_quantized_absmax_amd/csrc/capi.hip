@@ -62,15 +62,17 @@ size_t fwd_ws(int64_t M, int64_t K, int32_t r) {
 
 // Workspace of the backward pass: T (recompute) | G | dA partials | dB partials.
 struct BwdWs {
-  size_t t, g, pa, pb, total;
+  size_t t, g, bt, pa, pb, total;
 };
+// Workspace of the backward pass: T (recompute) | G | B^T | dA partials | dB partials.
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w;
   w.t = bf16_bytes(M * r);
   w.g = bf16_bytes(M * r);
+  w.bt = lora_grad_in_ws_bytes(static_cast<int>(N), r);
   w.pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
   w.pb = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r), 256);
-  w.total = w.t + w.g + w.pa + w.pb;
+  w.total = w.t + w.g + w.bt + w.pa + w.pb;
   return w;
 }
 
@@ -138,14 +140,20 @@ int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, 
                                    static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_lora_grad_in_workspace_bytes(int64_t N, int32_t r) {
+  if (N < 8 || N % 8 || N > kMaxElems / 128 || r < 1 || r > 128) return 0;
+  return lora_grad_in_ws_bytes(static_cast<int>(N), r);
+}
+
 int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r, float scale,
-                       uint16_t *G, void *stream) {
+                       uint16_t *G, void *ws, size_t ws_bytes, void *stream) {
   if (M < 0 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
   if (N < 8 || N % 8 || r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
-  if (M > kMaxElems / N) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M > kMaxElems / N || N > kMaxElems / 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!bf16_ok(dY) || !bf16_ok(B) || !bf16_ok(G)) return QLORA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grad_in_workspace_bytes(N, r)) return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;
-  return from_hip(launch_lora_grad_in(dY, static_cast<int>(M), static_cast<int>(N), B, r, scale, G,
+  return from_hip(launch_lora_grad_in(dY, static_cast<int>(M), static_cast<int>(N), B, r, scale, G, ws,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -180,6 +188,7 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
                      void *stream) {
   if (M < 0 || N < 1 || K < 1) return QLORA_ERR_INVALID_ARG;
   if (r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if ((dA && (K < 8 || K % 8)) || (dB && (N < 8 || N % 8))) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > 0 && M > kMaxElems / std::max(N, K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
   if (dA && (!bf16_ok(X) || !bf16_ok(G))) return QLORA_ERR_INVALID_ARG;
@@ -314,11 +323,12 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
   char *base = static_cast<char *>(ws);
   uint16_t *Tw = reinterpret_cast<uint16_t *>(base);
   uint16_t *G = reinterpret_cast<uint16_t *>(base + L.t);
-  void *pa = base + L.t + L.g;
-  void *pb = base + L.t + L.g + L.pa;
+  void *bt = base + L.t + L.g;
+  void *pa = base + L.t + L.g + L.bt;
+  void *pb = base + L.t + L.g + L.bt + L.pa;
   hipError_t e = hipSuccess;
   if (dX || dA) {
-    e = launch_lora_grad_in(dY, m, v.N, B, r, scale, G, s);
+    e = launch_lora_grad_in(dY, m, v.N, B, r, scale, G, bt, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dX) {

@@ -92,14 +92,17 @@ hipError_t launch_small_m_fwd(const uint16_t *X, int M, const NF4View &w, const 
 hipError_t launch_matmul_dx(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
                             const uint16_t *A, int r, uint16_t *dX, hipStream_t s);
 
-// ---- LoRA skinny products ------------------------------------------------------
-// T [M, r] = scale X [M, K] A^T  (A [r, K])
+// ---- LoRA products ------------------------------------------------------------
+// T [M, r] = scale X [M, K] A^T  (A [r, K]); K % 8 == 0.
 hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, float scale,
                             uint16_t *T, hipStream_t s);
-// G [M, r] = scale dY [M, N] B  (B [N, r])
+// G [M, r] = scale dY [M, N] B  (B [N, r]); N % 8 == 0; ws (lora_grad_in_ws_bytes)
+// holds a zero-padded copy of B when r % 8 != 0.
+size_t lora_grad_in_ws_bytes(int N, int r);
 hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r, float scale,
-                               uint16_t *G, hipStream_t s);
-// out = P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB).
+                               uint16_t *G, void *ws, hipStream_t s);
+// out = P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB);
+// D % 8 == 0; ws (lora_grad_ws_bytes): padded Q (r % 8 != 0) | split partials.
 size_t lora_grad_ws_bytes(int M, int D, int r);
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s);

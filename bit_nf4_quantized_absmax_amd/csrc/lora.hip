@@ -4,15 +4,38 @@
 // 16-bit while the base stays frozen (automatone.win, "QLoRA paper
 // explained", The problem and How it works; creativeworksofknowledge.com,
 // "QLoRA: Fine-Tune 70B on One GPU", Code: r, lora_alpha).  With A [r, K],
-// B [N, r]:
-//   k_skinny_nt<false>   T = s X A^T   (contraction over K, both K-contiguous)
-//   k_skinny_nt<true>    G = s dY B    (contraction over N; B read transposed)
-//   k_grad_partial       P^T Q over an M-slice -> fp32 partials
-//   k_grad_reduce        fixed-order sum of the partials, bf16 out
-// with (P, Q) = (X, G) for dA = s G0^T X [r, K] and (dY, T) for
-// dB = s dY^T T0 [N, r], where T0, G0 are the unscaled products: the scale
-// s = alpha / r is applied once, in fp32, before T and G are rounded to bf16.
-// These are streaming products: each reads its wide operand (X or dY) once.
+// B [N, r] and s = alpha / r:
+//   k_lora_nt   T = s X A^T  [M, r]   contraction over K (A rows read as is)
+//               G = s dY B   [M, r]   contraction over N (B read transposed)
+//   k_lora_tn   dA = G^T X   [r, K]   contraction over M (both read transposed)
+//               dB = dY^T T  [N, r]
+//   k_sum_partials   fixed-order sum of the M-split partials of k_lora_tn
+// G and T carry the scale, which is applied once, in fp32, before T and G are
+// rounded to bf16.  These are streaming products: each reads its wide operand
+// (X or dY) once from HBM.
+//
+// Common design (both products):
+//  * Operand tiles go global -> LDS with 16-byte DMA loads
+//    (global_load_lds_dwordx4), eight 128-byte rows (1 KB) per instruction,
+//    16-byte chunks XOR-swizzled by row.  Every wave owns a private ring of
+//    stages in LDS and keeps several stages in flight; waves take interleaved
+//    stages of the contraction and are summed in LDS in wave order at the end
+//    (deterministic).  There is no barrier in the main loop.
+//  * MFMA operands are read from LDS by inline-asm blocks that also wait for
+//    their own data: the compiler then sees no LDS read of DMA-written memory,
+//    which it would otherwise guard with conservative vmcnt(0) waits; the
+//    waits on the DMA stream (vmcnt, in issue order) are explicit.
+//  * A contraction-major operand (B [N, r], X, dY, G, T with the contraction
+//    over rows) is read with ds_read_b64_tr_b16: within each group of 16
+//    lanes, lane i receives element i % 4 of the 8-byte reads of lanes
+//    i / 4 + 4 e (e = 0..3).  Pointing source lane t at row t / 4 and columns
+//    4 (t % 4) .. +3 of a 4 x 16 block hands lane i column i of that block, 4
+//    consecutive rows: two such reads make one MFMA operand of 8 consecutive
+//    contraction indices, with no transpose pass through memory.
+//  * Each workgroup starts its walk over the contraction at a different
+//    stage, so that concurrent workgroups do not all read the same column band
+//    of row-major operands whose row pitch is a power of two (which
+//    concentrates the traffic on a few HBM channels).
 #include <algorithm>
 
 #include "common.h"
@@ -20,300 +43,634 @@
 
 namespace qlora {
 
-constexpr int kSkThreads = 512;   // 8 waves, each a slice of the contraction
-constexpr int kSkRows = 32;       // output rows per workgroup
+#define QLORA_LORA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-// out[m][j] = scale * sum_k L[m][k] R(j, k) for m in a 32-row tile, j < r, where
-// R(j, k) = Rm[j * ldr + k] (kTransR = false, Rm = A [r, K]) or
-// R(j, k) = Rm[k * r + j] (kTransR = true, Rm = B [N, r]).
-// Wave w takes contraction steps of 32 with index w, w + 8, ...; the 8 wave
-// partials are summed in LDS in wave order (deterministic).
-template <bool kTransR, int kRP>
-__global__ __launch_bounds__(kSkThreads) void k_skinny_nt(const uint16_t *__restrict__ L, int M, int Kc,
-                                                          const uint16_t *__restrict__ Rm, int r, float scale,
-                                                          uint16_t *__restrict__ out) {
-  constexpr int kJB = kRP / 16;
-  __shared__ float red[8][kSkRows][kRP + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  const int m0 = blockIdx.x * kSkRows;
+namespace {
 
-  f32x4_t acc[2][kJB];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < kJB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+constexpr int kLoWaves = 4;     // waves per workgroup, one per SIMD
+constexpr int kLoThreads = kLoWaves * 64;
 
-  // Kc % 8 == 0: an 8-element chunk is wholly inside or wholly past Kc.
-  const int steps = (Kc + 31) / 32;
-  for (int st = wave; st < steps; st += 8) {
-    const int k = st * 32 + lk;
-    const bool kin = k < Kc;
-    bf16x8_t av[2], bv[kJB];
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n), other counters not waited.
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Tiles have 128-byte rows (64 bf16); chunk c of row `row` is stored at
+// 16-byte position c ^ swz_f(row).
+__device__ __forceinline__ int swz_f(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 16 * (chunk ^ swz_f(row)); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t *)(p)));
+}
+
+// DMA rows row0 .. row0 + kRows - 1 and columns col0 .. col0 + 63 of a bf16
+// matrix (row pitch ld elements, 16-byte aligned rows) into a swizzled tile.
+// Rows past nrows are clamped to row nrows - 1 and chunks past ncols to the
+// row's last chunk (ncols % 8 == 0): finite data that the kernels mask or
+// never store.  Lane i of instruction u lands in slot i: row 8 u + i / 8,
+// position i % 8, i.e. logical chunk (i % 8) ^ swz_f(row).
+template <int kRows>
+__device__ __forceinline__ void dma_tile(uint8_t *dst, const uint16_t *src, int64_t ld, int row0, int nrows,
+                                         int col0, int ncols, int lane) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = m0 + i * 16 + lrow;
-      if (m < M && kin)
-        av[i] = *reinterpret_cast<const bf16x8_t *>(L + static_cast<int64_t>(m) * Kc + k);
-      else
-        av[i] = bf16x8_t{};
-    }
-#pragma unroll
-    for (int j = 0; j < kJB; ++j) {
-      const int jr = j * 16 + lrow;
-      if (jr < r && kin) {
-        if (!kTransR) {
-          bv[j] = *reinterpret_cast<const bf16x8_t *>(Rm + static_cast<int64_t>(jr) * Kc + k);
-        } else {
-          uint16_t t[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) t[e] = Rm[static_cast<int64_t>(k + e) * r + jr];
-          bv[j] = __builtin_bit_cast(bf16x8_t, t);
-        }
-      } else {
-        bv[j] = bf16x8_t{};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < kJB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  for (int u = 0; u < kRows / 8; ++u) {
+    const int row = 8 * u + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_f(row);
+    const int grow = min(row0 + row, nrows - 1);
+    const int gcol = min(col0 + 8 * chunk, ncols - 8);
+    __builtin_amdgcn_global_load_lds(src + static_cast<int64_t>(grow) * ld + gcol, QLORA_LORA_LDS(dst + u * 1024),
+                                     16, 0, 0);
   }
+}
+
+// Byte offset, within a swizzled tile, of this lane's transposed-read source
+// for column block cb (32 columns) and half h of a 16-row sub-step (the
+// sub-step adds 2048 bytes): group G = lane / 16 covers columns
+// 32 cb + 16 (G % 2) .. +15 and rows 8 (G / 2) + 4 h .. +3; source lane
+// t = lane % 16 points at row t / 4 of those and columns 4 (t % 4) .. +3.
+__device__ __forceinline__ uint32_t tr_offset(int lane, int cb, int h) {
+  const int t = lane & 15, g = lane >> 4;
+  const int row = 8 * (g >> 1) + 4 * h + (t >> 2);
+  const int chunk = 4 * cb + 2 * (g & 1) + ((t & 3) >> 1);
+  return static_cast<uint32_t>(swz(row, chunk) + 8 * (t & 1));
+}
+
+__device__ __forceinline__ bf16x8_t join_tr(u32x2_t lo, u32x2_t hi) {
+  uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Zero the elements of an 8-element operand whose contraction index
+// (first + q, q = 0..7) is >= limit.
+__device__ __forceinline__ bf16x8_t mask_tail(bf16x8_t v, int first, int limit) {
+  uint4 u = __builtin_bit_cast(uint4, v);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = (first + 2 * q < limit) ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (first + 2 * q + 1 < limit) ? 0xFFFF0000u : 0u;
+    w[q] &= lo | hi;
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// ===========================================================================
+// k_lora_nt: out[m][j0 + j] = scale sum_k L[m][k] R(j, k), j < 64.
+//   kRT = false: R(j, k) = R[j][k]  (A [r, K]: 16-byte operand reads)
+//   kRT = true:  R(j, k) = R[k][j]  (B [N, r]: transposed reads)
+// Workgroup: 32 rows of L; wave w takes the 64-wide contraction stages
+// w, w + 4, ... (rotated per workgroup).  Stage = L tile [32 m][64 k] (4 KB)
+// + R tile (8 KB: [64 j][64 k] or [64 k][64 j]).  MFMA 32x32x16: lane l
+// supplies row l % 32 of the L tile and column l % 32 (+ 32 jb) of the R side
+// with contraction elements 8 (l / 32) .. +7 of each 16-wide sub-step.
+// ===========================================================================
+constexpr int kNtRows = 32;
+constexpr int kNtSlots = 3;
+constexpr int kNtLB = kNtRows * 128;          // L tile bytes
+constexpr int kNtRB = 64 * 128;               // R tile bytes
+constexpr int kNtStage = kNtLB + kNtRB;
+constexpr int kNtDma = kNtRows / 8 + 8;       // DMA instructions per stage
+
+template <bool kRT>
+struct NtStage {
+  bf16x8_t a[4], b0[4], b1[4];
+};
+
+// Operand reads of one stage at byte offset kOff of the wave's ring.
+// vo[s]: this lane's offset of sub-step s in an L tile (rows l % 32);
+// vt[jb][h]: transposed-read offsets in an R tile.
+template <int kOff>
+__device__ __forceinline__ void nt_read(const uint32_t (&vo)[4], const uint32_t (&vt)[2][2], NtStage<false> &st) {
+  asm volatile(
+      "ds_read_b128 %0, %12 offset:%16\n\t"
+      "ds_read_b128 %1, %12 offset:%17\n\t"
+      "ds_read_b128 %2, %12 offset:%18\n\t"
+      "ds_read_b128 %3, %13 offset:%16\n\t"
+      "ds_read_b128 %4, %13 offset:%17\n\t"
+      "ds_read_b128 %5, %13 offset:%18\n\t"
+      "ds_read_b128 %6, %14 offset:%16\n\t"
+      "ds_read_b128 %7, %14 offset:%17\n\t"
+      "ds_read_b128 %8, %14 offset:%18\n\t"
+      "ds_read_b128 %9, %15 offset:%16\n\t"
+      "ds_read_b128 %10, %15 offset:%17\n\t"
+      "ds_read_b128 %11, %15 offset:%18\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(st.a[0]), "=&v"(st.b0[0]), "=&v"(st.b1[0]), "=&v"(st.a[1]), "=&v"(st.b0[1]), "=&v"(st.b1[1]),
+        "=&v"(st.a[2]), "=&v"(st.b0[2]), "=&v"(st.b1[2]), "=&v"(st.a[3]), "=&v"(st.b0[3]), "=&v"(st.b1[3])
+      : "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "n"(kOff), "n"(kOff + kNtLB), "n"(kOff + kNtLB + 4096)
+      : "memory");
+  (void)vt;
+}
+
+template <int kOff, int kS0>
+__device__ __forceinline__ void nt_read_tr_half(const uint32_t (&vo)[4], const uint32_t (&vt)[2][2],
+                                                NtStage<true> &st) {
+  u32x2_t t[2][2][2];   // [sub-step][jb][h]
+  asm volatile(
+      "ds_read_b128 %0, %10 offset:%16\n\t"
+      "ds_read_b128 %1, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %12 offset:%17\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:%17\n\t"
+      "ds_read_b64_tr_b16 %4, %14 offset:%17\n\t"
+      "ds_read_b64_tr_b16 %5, %15 offset:%17\n\t"
+      "ds_read_b64_tr_b16 %6, %12 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %7, %13 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %8, %14 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %9, %15 offset:%18\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(st.a[kS0]), "=&v"(st.a[kS0 + 1]), "=&v"(t[0][0][0]), "=&v"(t[0][0][1]), "=&v"(t[0][1][0]),
+        "=&v"(t[0][1][1]), "=&v"(t[1][0][0]), "=&v"(t[1][0][1]), "=&v"(t[1][1][0]), "=&v"(t[1][1][1])
+      : "v"(vo[kS0]), "v"(vo[kS0 + 1]), "v"(vt[0][0]), "v"(vt[0][1]), "v"(vt[1][0]), "v"(vt[1][1]), "n"(kOff),
+        "n"(kOff + kNtLB + 2048 * kS0), "n"(kOff + kNtLB + 2048 * (kS0 + 1))
+      : "memory");
 #pragma unroll
-    for (int j = 0; j < kJB; ++j)
+  for (int s = 0; s < 2; ++s) {
+    st.b0[kS0 + s] = join_tr(t[s][0][0], t[s][0][1]);
+    st.b1[kS0 + s] = join_tr(t[s][1][0], t[s][1][1]);
+  }
+}
+
+template <int kOff>
+__device__ __forceinline__ void nt_read(const uint32_t (&vo)[4], const uint32_t (&vt)[2][2], NtStage<true> &st) {
+  nt_read_tr_half<kOff, 0>(vo, vt, st);
+  nt_read_tr_half<kOff, 2>(vo, vt, st);
+}
+
+template <bool kRT>
+__global__ __launch_bounds__(kLoThreads) void k_lora_nt(const uint16_t *__restrict__ L, int M, int Kc,
+                                                        const uint16_t *__restrict__ R, int rcols, int r,
+                                                        float scale, uint16_t *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kNtSlots][kNtStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = blockIdx.x * kNtRows;
+  const int j0 = blockIdx.y * 64;
+  const int nst = (Kc + 63) / 64;
+  const int n_i = nst > wave ? (nst - wave + kLoWaves - 1) / kLoWaves : 0;
+  const int rot = static_cast<int>(blockIdx.x % static_cast<unsigned>(nst));
+  // contraction offset of this wave's i-th stage (rotated, always < Kc for i < n_i)
+  auto kof = [&](int i) {
+    int t = wave + kLoWaves * i + rot;
+    if (t >= nst) t -= nst;
+    return t * 64;
+  };
+  uint8_t *ring = smem[wave][0];
+  auto issue = [&](int i, int slot) {
+    uint8_t *st = ring + slot * kNtStage;
+    const int k0 = kof(i);
+    dma_tile<kNtRows>(st, L, Kc, m0, M, k0, Kc, lane);
+    if (kRT)
+      dma_tile<64>(st + kNtLB, R, rcols, k0, Kc, j0, rcols, lane);   // rows k, columns j
+    else
+      dma_tile<64>(st + kNtLB, R, Kc, j0, rcols, k0, Kc, lane);      // rows j (rcols = rows of A), columns k
+  };
+
+  const uint32_t base = lds_addr(ring);
+  const int lr = lane & 31, lh = lane >> 5;
+  uint32_t vo[4], vt[2][2];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][i * 16 + (lane >> 4) * 4 + v][j * 16 + (lane & 15)] = acc[i][j][v];
+  for (int s = 0; s < 4; ++s) vo[s] = base + static_cast<uint32_t>(swz(lr, 2 * s + lh));
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vt[jb][h] = base + tr_offset(lane, jb, h);
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    acc[0][e] = 0.f;
+    acc[1][e] = 0.f;
+  }
+  auto compute = [&](int k0, const NtStage<kRT> &st) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8_t x = (k0 + 8 * (2 * s + lh) < Kc) ? st.a[s] : bf16x8_t{};
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, st.b0[s], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, st.b1[s], acc[1], 0, 0, 0);
+    }
+  };
+  // Stage i: issue stage i + 2 (if any), wait until stage i has landed (the
+  // younger stages, issued after it, may still be in flight), read, multiply.
+  auto wait_for = [&](int i) {
+    const int younger = min(n_i - 1 - i, 2);
+    if (younger >= 2)
+      __builtin_amdgcn_s_waitcnt(vm_wait(2 * kNtDma));
+    else if (younger == 1)
+      __builtin_amdgcn_s_waitcnt(vm_wait(kNtDma));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  };
+  if (n_i > 0) issue(0, 0);
+  if (n_i > 1) issue(1, 1);
+  int i = 0;
+  for (; i + 3 <= n_i; i += 3) {
+    NtStage<kRT> st;
+    if (i + 2 < n_i) issue(i + 2, 2);
+    wait_for(i);
+    nt_read<0>(vo, vt, st);
+    compute(kof(i), st);
+    if (i + 3 < n_i) issue(i + 3, 0);
+    wait_for(i + 1);
+    nt_read<kNtStage>(vo, vt, st);
+    compute(kof(i + 1), st);
+    if (i + 4 < n_i) issue(i + 4, 1);
+    wait_for(i + 2);
+    nt_read<2 * kNtStage>(vo, vt, st);
+    compute(kof(i + 2), st);
+  }
+  if (i < n_i) {   // tail: stages i (slot 0) and possibly i + 1 (slot 1), both already issued
+    NtStage<kRT> st;
+    wait_for(i);
+    nt_read<0>(vo, vt, st);
+    compute(kof(i), st);
+    if (i + 1 < n_i) {
+      wait_for(i + 1);
+      nt_read<kNtStage>(vo, vt, st);
+      compute(kof(i + 1), st);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+
+  // Wave partials (32 x 64 fp32) into the wave's own first slot, then the
+  // sum over waves in wave order.  MFMA 32x32 output: lane l holds column
+  // l % 32 of block jb; element e holds row 8 (e / 4) + 4 (l / 32) + e % 4.
+  float *red = reinterpret_cast<float *>(ring);
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[(8 * (e >> 2) + 4 * lh + (e & 3)) * 64 + 32 * jb + lr] = acc[jb][e];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kSkRows * kRP; idx += kSkThreads) {
-    const int row = idx / kRP, j = idx % kRP;
-    float s = red[0][row][j];
+  const int row = threadIdx.x >> 3, c = threadIdx.x & 7;
+  float sm[8];
 #pragma unroll
-    for (int w = 1; w < 8; ++w) s += red[w][row][j];
-    if (m0 + row < M && j < r) out[static_cast<int64_t>(m0 + row) * r + j] = f32_to_bf16(s * scale);
+  for (int q = 0; q < 8; ++q) sm[q] = reinterpret_cast<const float *>(smem[0][0])[row * 64 + 8 * c + q];
+#pragma unroll
+  for (int w = 1; w < kLoWaves; ++w)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sm[q] += reinterpret_cast<const float *>(smem[w][0])[row * 64 + 8 * c + q];
+  const int gm = m0 + row;
+  const int jl = j0 + 8 * c;
+  if (gm < M) {
+    uint16_t *o = out + static_cast<int64_t>(gm) * r + jl;
+    if (jl + 8 <= r && (r & 7) == 0) {
+      *reinterpret_cast<uint4 *>(o) =
+          make_uint4(pack_bf16x2(sm[0] * scale, sm[1] * scale), pack_bf16x2(sm[2] * scale, sm[3] * scale),
+                     pack_bf16x2(sm[4] * scale, sm[5] * scale), pack_bf16x2(sm[6] * scale, sm[7] * scale));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (jl + q < r) o[q] = f32_to_bf16(sm[q] * scale);
+    }
   }
 }
 
-template <bool kTransR>
-static hipError_t launch_skinny(const uint16_t *L, int M, int Kc, const uint16_t *R, int r, float scale,
-                                uint16_t *out, hipStream_t s) {
-  const dim3 grid((M + kSkRows - 1) / kSkRows);
-  if (r <= 64)
-    hipLaunchKernelGGL((k_skinny_nt<kTransR, 64>), grid, dim3(kSkThreads), 0, s, L, M, Kc, R, r, scale, out);
-  else
-    hipLaunchKernelGGL((k_skinny_nt<kTransR, 128>), grid, dim3(kSkThreads), 0, s, L, M, Kc, R, r, scale, out);
-  return hipGetLastError();
+// ===========================================================================
+// k_lora_tn: acc[j][d] = sum_m Q[m][j0 + j] P[m][d0 + d] over an M-split,
+// j, d < 64.  Workgroup (d-tile of 64, split): wave w takes the 32-row
+// stages w, w + 4, ... of the split (rotated per d-tile).  Stage = P tile
+// [32 m][64 d] + Q tile [32 m][64 j] (4 KB each); both MFMA operands come
+// from transposed reads (contraction over rows).  Output: bf16 directly
+// (one split) as [j][d] (dA) or [d][j] (dB), else fp32 partials of the same
+// orientation, summed by k_sum_partials.
+// ===========================================================================
+constexpr int kTnRows = 32;
+constexpr int kTnSlots = 4;
+constexpr int kTnTile = kTnRows * 128;      // 4 KB
+constexpr int kTnStage = 2 * kTnTile;       // P then Q
+constexpr int kTnDma = 2 * kTnRows / 8;     // DMA instructions per stage
+constexpr int kTnRedPitch = 65;             // floats per row of a wave's 64 x 64 partial
+
+struct TnStage {
+  bf16x8_t q[2][2], p[2][2];   // [sub-step][column block]
+};
+
+template <int kOff>
+__device__ __forceinline__ void tn_read(const uint32_t (&vt)[2][2], TnStage &st) {
+  u32x2_t t[2][2][2][2];   // [tile: Q, P][sub-step][cb][h]
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %1, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %3, %19 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %14, %18 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0][0][0]), "=&v"(t[0][0][0][1]), "=&v"(t[0][0][1][0]), "=&v"(t[0][0][1][1]),
+        "=&v"(t[0][1][0][0]), "=&v"(t[0][1][0][1]), "=&v"(t[0][1][1][0]), "=&v"(t[0][1][1][1]),
+        "=&v"(t[1][0][0][0]), "=&v"(t[1][0][0][1]), "=&v"(t[1][0][1][0]), "=&v"(t[1][0][1][1]),
+        "=&v"(t[1][1][0][0]), "=&v"(t[1][1][0][1]), "=&v"(t[1][1][1][0]), "=&v"(t[1][1][1][1])
+      : "v"(vt[0][0]), "v"(vt[0][1]), "v"(vt[1][0]), "v"(vt[1][1]), "n"(kOff + kTnTile),
+        "n"(kOff + kTnTile + 2048), "n"(kOff), "n"(kOff + 2048)
+      : "memory");
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      st.q[s][cb] = join_tr(t[0][s][cb][0], t[0][s][cb][1]);
+      st.p[s][cb] = join_tr(t[1][s][cb][0], t[1][s][cb][1]);
+    }
 }
+
+__global__ __launch_bounds__(kLoThreads) void k_lora_tn(const uint16_t *__restrict__ P, int M, int D,
+                                                        const uint16_t *__restrict__ Q, int qcols, int r,
+                                                        int stages_per_split, bool out_j_major,
+                                                        uint16_t *__restrict__ out, float *__restrict__ part,
+                                                        int64_t part_plane, int part_pitch) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kTnSlots][kTnStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int d0 = blockIdx.x * 64;
+  const int sp = blockIdx.y;
+  const int j0 = blockIdx.z * 64;
+  const int nms = (M + kTnRows - 1) / kTnRows;
+  const int sbeg = sp * stages_per_split;
+  const int count = max(0, min(nms, sbeg + stages_per_split) - sbeg);
+  const int mend = min(M, (sbeg + count) * kTnRows);
+  const int n_i = count > wave ? (count - wave + kLoWaves - 1) / kLoWaves : 0;
+  const int rot = count > 0 ? static_cast<int>(blockIdx.x % static_cast<unsigned>(count)) : 0;
+  auto mof = [&](int i) {
+    int t = wave + kLoWaves * i + rot;
+    if (t >= count) t -= count;
+    return (sbeg + t) * kTnRows;
+  };
+  uint8_t *ring = smem[wave][0];
+  auto issue = [&](int i, int slot) {
+    uint8_t *st = ring + slot * kTnStage;
+    const int m0 = mof(i);
+    dma_tile<kTnRows>(st, P, D, m0, M, d0, D, lane);
+    dma_tile<kTnRows>(st + kTnTile, Q, qcols, m0, M, j0, qcols, lane);
+  };
+  const uint32_t base = lds_addr(ring);
+  const int lr = lane & 31, lh = lane >> 5;
+  uint32_t vt[2][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vt[cb][h] = base + tr_offset(lane, cb, h);
+
+  f32x16_t acc[2][2];   // [jb][db]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  auto compute = [&](int m0, TnStage &st) {
+    if (m0 + kTnRows > mend) {   // rows past the split (or M) contribute zero
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) st.q[s][cb] = mask_tail(st.q[s][cb], m0 + 16 * s + 8 * lh, mend);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          acc[jb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.q[s][jb], st.p[s][db], acc[jb][db], 0, 0, 0);
+  };
+  auto wait_for = [&](int i) {
+    const int younger = min(n_i - 1 - i, 3);
+    if (younger >= 3)
+      __builtin_amdgcn_s_waitcnt(vm_wait(3 * kTnDma));
+    else if (younger == 2)
+      __builtin_amdgcn_s_waitcnt(vm_wait(2 * kTnDma));
+    else if (younger == 1)
+      __builtin_amdgcn_s_waitcnt(vm_wait(kTnDma));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  };
+  if (n_i > 0) issue(0, 0);
+  if (n_i > 1) issue(1, 1);
+  if (n_i > 2) issue(2, 2);
+  int i = 0;
+  for (; i + 4 <= n_i; i += 4) {
+    TnStage st;
+    if (i + 3 < n_i) issue(i + 3, 3);
+    wait_for(i);
+    tn_read<0>(vt, st);
+    compute(mof(i), st);
+    if (i + 4 < n_i) issue(i + 4, 0);
+    wait_for(i + 1);
+    tn_read<kTnStage>(vt, st);
+    compute(mof(i + 1), st);
+    if (i + 5 < n_i) issue(i + 5, 1);
+    wait_for(i + 2);
+    tn_read<2 * kTnStage>(vt, st);
+    compute(mof(i + 2), st);
+    if (i + 6 < n_i) issue(i + 6, 2);
+    wait_for(i + 3);
+    tn_read<3 * kTnStage>(vt, st);
+    compute(mof(i + 3), st);
+  }
+  if (i < n_i) {   // tail: up to three stages, already issued into slots 0, 1, 2
+    TnStage st;
+    wait_for(i);
+    tn_read<0>(vt, st);
+    compute(mof(i), st);
+    if (i + 1 < n_i) {
+      wait_for(i + 1);
+      tn_read<kTnStage>(vt, st);
+      compute(mof(i + 1), st);
+    }
+    if (i + 2 < n_i) {
+      wait_for(i + 2);
+      tn_read<2 * kTnStage>(vt, st);
+      compute(mof(i + 2), st);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+
+  // Wave partials: acc[jb][db][e] at lane l is (j, d) =
+  // (32 jb + 8 (e / 4) + 4 (l / 32) + e % 4, 32 db + l % 32); stored as
+  // red[j * 65 + d] in the wave's own ring, then summed in wave order.
+  float *red = reinterpret_cast<float *>(ring);
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        red[(32 * jb + 8 * (e >> 2) + 4 * lh + (e & 3)) * kTnRedPitch + 32 * db + lr] = acc[jb][db][e];
+  __syncthreads();
+  // thread t: output row t / 4 of the orientation, 16 consecutive columns
+  const int orow = threadIdx.x >> 2, oc0 = 16 * (threadIdx.x & 3);
+  float sm[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int j = out_j_major ? orow : oc0 + q;
+    const int d = out_j_major ? oc0 + q : orow;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kLoWaves; ++w) v += reinterpret_cast<const float *>(smem[w][0])[j * kTnRedPitch + d];
+    sm[q] = v;
+  }
+  // global (row, column) of this thread's first element, and the bounds
+  const int grow = out_j_major ? j0 + orow : d0 + orow;
+  const int gcol = out_j_major ? d0 + oc0 : j0 + oc0;
+  const int nrow = out_j_major ? r : D;
+  const int ncol = out_j_major ? D : r;
+  if (grow >= nrow) return;
+  if (part) {
+    float *dst = part + sp * part_plane + static_cast<int64_t>(grow) * part_pitch + gcol;
+#pragma unroll
+    for (int q = 0; q < 16; q += 4)
+      *reinterpret_cast<float4 *>(dst + q) = make_float4(sm[q], sm[q + 1], sm[q + 2], sm[q + 3]);
+  } else {
+    uint16_t *dst = out + static_cast<int64_t>(grow) * ncol + gcol;
+    if (gcol + 16 <= ncol && (ncol & 7) == 0) {
+#pragma unroll
+      for (int q = 0; q < 16; q += 8)
+        *reinterpret_cast<uint4 *>(dst + q) =
+            make_uint4(pack_bf16x2(sm[q], sm[q + 1]), pack_bf16x2(sm[q + 2], sm[q + 3]),
+                       pack_bf16x2(sm[q + 4], sm[q + 5]), pack_bf16x2(sm[q + 6], sm[q + 7]));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (gcol + q < ncol) dst[q] = f32_to_bf16(sm[q]);
+    }
+  }
+}
+
+// out[row][col] = bf16(sum_sp part[sp][row][col]) (splits in order).
+__global__ __launch_bounds__(256) void k_sum_partials(const float *__restrict__ part, int splits,
+                                                      int64_t plane, int pitch, int nrow, int ncol,
+                                                      uint16_t *__restrict__ out) {
+  const int64_t total = static_cast<int64_t>(nrow) * ncol;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * 256) {
+    const int row = static_cast<int>(idx / ncol), col = static_cast<int>(idx % ncol);
+    const float *p = part + static_cast<int64_t>(row) * pitch + col;
+    float s = p[0];
+    for (int sp = 1; sp < splits; ++sp) s += p[sp * plane];
+    out[idx] = f32_to_bf16(s);
+  }
+}
+
+// dst [rows, rq] = src [rows, r] with zero columns r .. rq - 1 (rq = r rounded
+// up to 8): 16-byte aligned rows for the DMA tiles.
+__global__ __launch_bounds__(256) void k_pad_cols(const uint16_t *__restrict__ src, int rows, int r, int rq,
+                                                  uint16_t *__restrict__ dst) {
+  const int64_t total = static_cast<int64_t>(rows) * rq;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t row = idx / rq;
+    const int col = static_cast<int>(idx % rq);
+    dst[idx] = col < r ? src[row * r + col] : static_cast<uint16_t>(0);
+  }
+}
+
+int round8(int r) { return (r + 7) & ~7; }
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+unsigned grid_for(int64_t total) { return static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 4096)); }
+
+// Pads an r-column matrix into ws when r % 8 != 0; returns the matrix to use
+// and its column count.
+const uint16_t *padded(const uint16_t *src, int rows, int r, void *ws, int &cols, hipStream_t s) {
+  if ((r & 7) == 0) {
+    cols = r;
+    return src;
+  }
+  cols = round8(r);
+  uint16_t *dst = static_cast<uint16_t *>(ws);
+  hipLaunchKernelGGL(k_pad_cols, dim3(grid_for(static_cast<int64_t>(rows) * cols)), dim3(256), 0, s, src, rows, r,
+                     cols, dst);
+  return dst;
+}
+
+// M-splits of k_lora_tn: enough workgroups to cover the 256 compute units in
+// whole rounds (one workgroup per CU: the LDS ring is 128 KB), at least 8
+// stages per split, a small penalty per extra split for the partial traffic.
+int tn_splits(int M, int D) {
+  const int dt = (D + 63) / 64;
+  const int nms = (M + kTnRows - 1) / kTnRows;
+  int best = 1;
+  double best_score = -1.0;
+  for (int sp = 1; sp <= 8; ++sp) {
+    if (sp > 1 && nms / sp < 8) break;
+    const int wg = dt * sp;
+    const int rounds = (wg + 255) / 256;
+    const double score = static_cast<double>(wg) / (256.0 * rounds) - 0.03 * (sp - 1);
+    if (score > best_score + 1e-9) {
+      best = sp;
+      best_score = score;
+    }
+  }
+  return best;
+}
+
+}  // namespace
 
 hipError_t launch_lora_down(const uint16_t *X, int M, int K, const uint16_t *A, int r, float scale, uint16_t *T,
                             hipStream_t s) {
-  return launch_skinny<false>(X, M, K, A, r, scale, T, s);
+  const dim3 grid((M + kNtRows - 1) / kNtRows, (r + 63) / 64);
+  hipLaunchKernelGGL((k_lora_nt<false>), grid, dim3(kLoThreads), 0, s, X, M, K, A, r, r, scale, T);
+  return hipGetLastError();
+}
+
+size_t lora_grad_in_ws_bytes(int N, int r) {
+  return (r & 7) ? align256(static_cast<size_t>(N) * round8(r) * 2) : 256;
 }
 
 hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r, float scale,
-                               uint16_t *G, hipStream_t s) {
-  return launch_skinny<true>(dY, M, N, B, r, scale, G, s);
+                               uint16_t *G, void *ws, hipStream_t s) {
+  int cols = 0;
+  const uint16_t *Bp = padded(B, N, r, ws, cols, s);
+  const dim3 grid((M + kNtRows - 1) / kNtRows, (r + 63) / 64);
+  hipLaunchKernelGGL((k_lora_nt<true>), grid, dim3(kLoThreads), 0, s, dY, M, N, Bp, cols, r, scale, G);
+  return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// dA / dB: out = P^T Q over M, P [M, D] (X or dY), Q [M, r] (G or T, already
-// carrying the scale).  The contraction runs over M, which is the slow index
-// of both operands, so:
-//  * Q is first transposed into Qt [r, Mp] (k_transpose_narrow, Mp = M
-//    rounded up to 8) so that 8 consecutive m of one column are one 16-byte
-//    load;
-//  * each lane loads an 8 (m) x 8 (d) block of P with eight 16-byte loads
-//    and transposes it in registers (32 v_perm), giving eight MFMA operands
-//    of 8 consecutive m for 8 different d.
-// Workgroup (d-tile of 128, M-split sp): 4 waves take interleaved 32-row
-// sub-steps of the split; MFMA 16x16x32 with A-row i of fragment f holding
-// d = d0 + 8 i + f.  The 4 wave partials are summed in LDS in wave order and
-// the split partials by k_grad_reduce in split order (deterministic).
-// ---------------------------------------------------------------------------
-constexpr int kGrThreads = 256;
-constexpr int kGrD = 128;     // d per workgroup (16 lanes x 8)
-constexpr int kGrSub = 32;    // m per MFMA sub-step
-
-static int grad_splits(int M, int D) {
-  const int dt = (D + kGrD - 1) / kGrD;
-  int sp = (512 + dt - 1) / dt;
-  const int msteps = (M + 4 * kGrSub - 1) / (4 * kGrSub);
-  if (sp > msteps) sp = msteps;
-  if (sp < 1) sp = 1;
-  return sp;
-}
-
-static int padded_m(int M) { return (M + 7) & ~7; }
-
-// Qt [rp, Mp] from Q [M, r] (rows j >= r and columns m >= M are zero).
-__global__ __launch_bounds__(256) void k_transpose_narrow(const uint16_t *__restrict__ Q, int M, int r, int rp,
-                                                          int Mp, uint16_t *__restrict__ Qt) {
-  __shared__ uint16_t tile[64][129];
-  const int m0 = blockIdx.x * 128;
-  for (int idx = threadIdx.x; idx < 128 * 64; idx += 256) {
-    const int mm = idx >> 6, j = idx & 63;
-    const int m = m0 + mm;
-    tile[j][mm] = (m < M && j < r) ? Q[static_cast<int64_t>(m) * r + j] : static_cast<uint16_t>(0);
-  }
-  __syncthreads();
-  for (int jb = 0; jb < rp; jb += 64) {
-    if (jb > 0) {
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < 128 * 64; idx += 256) {
-        const int mm = idx >> 6, j = idx & 63;
-        const int m = m0 + mm;
-        tile[j][mm] = (m < M && jb + j < r) ? Q[static_cast<int64_t>(m) * r + jb + j] : static_cast<uint16_t>(0);
-      }
-      __syncthreads();
-    }
-    for (int idx = threadIdx.x; idx < 64 * 128; idx += 256) {
-      const int j = idx >> 7, mm = idx & 127;
-      const int m = m0 + mm;
-      if (m < Mp) Qt[static_cast<int64_t>(jb + j) * Mp + m] = tile[j][mm];
-    }
-  }
-}
-
-template <int kRP>
-__global__ __launch_bounds__(kGrThreads) void k_grad_partial(const uint16_t *__restrict__ P,
-                                                             const uint16_t *__restrict__ Qt, int M, int Mp,
-                                                             int D, int rows_per_split, float *__restrict__ part) {
-  constexpr int kJB = kRP / 16;
-  __shared__ float red[kGrD][kRP + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int d0 = blockIdx.x * kGrD;
-  const int sp = blockIdx.y;
-  const int mbeg = sp * rows_per_split;
-  const int mend = min(M, mbeg + rows_per_split);
-  const int dl = d0 + 8 * (lane & 15);     // this lane's 8 d columns
-  const int mg = 8 * (lane >> 4);          // this lane's 8-row group within the sub-step
-
-  f32x4_t acc[8][kJB];
-#pragma unroll
-  for (int f = 0; f < 8; ++f)
-#pragma unroll
-    for (int j = 0; j < kJB; ++j) acc[f][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int m0 = mbeg + wave * kGrSub; m0 < mend; m0 += 4 * kGrSub) {
-    // P block: rows m0 + mg .. +7, columns dl .. dl+7 (zero outside)
-    uint32_t v[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + mg + i;
-      uint4 t = make_uint4(0, 0, 0, 0);
-      if (m < mend && dl < D) t = *reinterpret_cast<const uint4 *>(P + static_cast<int64_t>(m) * D + dl);
-      v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
-    }
-    // 8 x 8 transpose of 16-bit elements: a[f] dword p = (P[2p][f], P[2p+1][f])
-    uint32_t a[8][4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        a[2 * c][p] = __builtin_amdgcn_perm(v[2 * p + 1][c], v[2 * p][c], 0x05040100u);
-        a[2 * c + 1][p] = __builtin_amdgcn_perm(v[2 * p + 1][c], v[2 * p][c], 0x07060302u);
-      }
-    // Qt fragments: column j = 16 jb + lane % 16, the lane's 8 rows of m
-    bf16x8_t b[kJB];
-#pragma unroll
-    for (int jb = 0; jb < kJB; ++jb) {
-      const int m = m0 + mg;
-      uint4 t = make_uint4(0, 0, 0, 0);
-      if (m < Mp) t = *reinterpret_cast<const uint4 *>(Qt + static_cast<int64_t>(16 * jb + (lane & 15)) * Mp + m);
-      b[jb] = __builtin_bit_cast(bf16x8_t, t);
-    }
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[f]);
-#pragma unroll
-      for (int jb = 0; jb < kJB; ++jb)
-        acc[f][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b[jb], acc[f][jb], 0, 0, 0);
-    }
-  }
-  // acc[f][jb][e] at lane l: d = d0 + 8 (4 (l / 16) + e) + f, j = 16 jb + l % 16.
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int f = 0; f < 8; ++f)
-#pragma unroll
-        for (int jb = 0; jb < kJB; ++jb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int dd = 8 * (4 * (lane >> 4) + e) + f, j = 16 * jb + (lane & 15);
-            if (w == 0)
-              red[dd][j] = acc[f][jb][e];
-            else
-              red[dd][j] += acc[f][jb][e];
-          }
-    }
-    __syncthreads();
-  }
-  const int dpad = gridDim.x * kGrD;
-  float *dst = part + static_cast<int64_t>(sp) * dpad * kRP;
-  for (int idx = threadIdx.x; idx < kGrD * kRP; idx += kGrThreads) {
-    const int dd = idx / kRP, j = idx % kRP;
-    dst[static_cast<int64_t>(d0 + dd) * kRP + j] = red[dd][j];
-  }
-}
-
-template <int kRP>
-__global__ __launch_bounds__(256) void k_grad_reduce(const float *__restrict__ part, int splits, int D, int dpad,
-                                                     int r, bool out_r_major, uint16_t *__restrict__ out) {
-  const int64_t total = static_cast<int64_t>(D) * r;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * 256) {
-    int d, j;
-    if (out_r_major) {   // consecutive threads write consecutive d of one j row
-      j = static_cast<int>(idx / D);
-      d = static_cast<int>(idx % D);
-    } else {
-      d = static_cast<int>(idx / r);
-      j = static_cast<int>(idx % r);
-    }
-    float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += part[(static_cast<int64_t>(sp) * dpad + d) * kRP + j];
-    const uint16_t v = f32_to_bf16(s);
-    if (out_r_major)
-      out[static_cast<int64_t>(j) * D + d] = v;
-    else
-      out[static_cast<int64_t>(d) * r + j] = v;
-  }
-}
-
-// workspace: Qt [rp, Mp] bf16 (256-byte aligned) | partials [splits, dpad, rp] fp32
+// workspace: [padded Q (r % 8 != 0)] | [fp32 partials (more than one split)]
 size_t lora_grad_ws_bytes(int M, int D, int r) {
-  const int rp = r <= 64 ? 64 : 128;
-  const int dt = (D + kGrD - 1) / kGrD;
-  const size_t qt = ((static_cast<size_t>(rp) * padded_m(M) * 2 + 255) / 256) * 256;
-  return qt + static_cast<size_t>(grad_splits(M, D)) * dt * kGrD * rp * sizeof(float);
+  const size_t pad = (r & 7) ? align256(static_cast<size_t>(M) * round8(r) * 2) : 0;
+  const int sp = tn_splits(M, D);
+  const int jc = (r + 63) / 64;
+  const size_t part = sp > 1 ? align256(static_cast<size_t>(sp) * (64 * jc) * (((D + 63) / 64) * 64) * 4) : 0;
+  return std::max<size_t>(pad + part, 256);
 }
 
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s) {
-  const int rp = r <= 64 ? 64 : 128;
-  const int Mp = padded_m(M);
-  const int sp = grad_splits(M, D);
-  const int dt = (D + kGrD - 1) / kGrD;
-  const int msteps = (M + kGrSub - 1) / kGrSub;
-  const int rows_per_split = ((msteps + sp - 1) / sp) * kGrSub;
-  uint16_t *Qt = static_cast<uint16_t *>(ws);
-  const size_t qt = ((static_cast<size_t>(rp) * Mp * 2 + 255) / 256) * 256;
-  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + qt);
-  hipLaunchKernelGGL(k_transpose_narrow, dim3((Mp + 127) / 128), dim3(256), 0, s, Q, M, r, rp, Mp, Qt);
-  const int64_t total = static_cast<int64_t>(D) * r;
-  const unsigned rgrid = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 4096));
-  if (rp == 64) {
-    hipLaunchKernelGGL(k_grad_partial<64>, dim3(dt, sp), dim3(kGrThreads), 0, s, P, Qt, M, Mp, D, rows_per_split,
-                       part);
-    hipLaunchKernelGGL(k_grad_reduce<64>, dim3(rgrid), dim3(256), 0, s, part, sp, D, dt * kGrD, r, out_r_major, out);
-  } else {
-    hipLaunchKernelGGL(k_grad_partial<128>, dim3(dt, sp), dim3(kGrThreads), 0, s, P, Qt, M, Mp, D, rows_per_split,
-                       part);
-    hipLaunchKernelGGL(k_grad_reduce<128>, dim3(rgrid), dim3(256), 0, s, part, sp, D, dt * kGrD, r, out_r_major,
-                       out);
+  const size_t pad = (r & 7) ? align256(static_cast<size_t>(M) * round8(r) * 2) : 0;
+  int qcols = 0;
+  const uint16_t *Qp = padded(Q, M, r, ws, qcols, s);
+  const int sp = tn_splits(M, D);
+  const int jc = (r + 63) / 64;
+  const int dt = (D + 63) / 64;
+  const int nms = (M + kTnRows - 1) / kTnRows;
+  const int per = (nms + sp - 1) / sp;
+  const dim3 grid(dt, sp, jc);
+  if (sp == 1) {
+    hipLaunchKernelGGL(k_lora_tn, grid, dim3(kLoThreads), 0, s, P, M, D, Qp, qcols, r, per, out_r_major, out,
+                       static_cast<float *>(nullptr), static_cast<int64_t>(0), 0);
+    return hipGetLastError();
   }
+  // partial planes in the output orientation: [64 jc, dt * 64] or [dt * 64, 64 jc]
+  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + pad);
+  const int prow = out_r_major ? 64 * jc : dt * 64;
+  const int pcol = out_r_major ? dt * 64 : 64 * jc;
+  const int64_t plane = static_cast<int64_t>(prow) * pcol;
+  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kLoThreads), 0, s, P, M, D, Qp, qcols, r, per, out_r_major,
+                     static_cast<uint16_t *>(nullptr), part, plane, pcol);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrow = out_r_major ? r : D, ncol = out_r_major ? D : r;
+  hipLaunchKernelGGL(k_sum_partials, dim3(grid_for(static_cast<int64_t>(nrow) * ncol)), dim3(256), 0, s, part, sp,
+                     plane, pcol, nrow, ncol, out);
   return hipGetLastError();
 }
 

@@ -225,15 +225,19 @@ def nf4_matmul_fwd(X, w, T, B, out=None):
     return Y
 
 
-def lora_grad_in(dY, B, scale, out=None):
+def lora_grad_in(dY, B, scale, out=None, workspace=None):
     """G = scale dY B."""
     M, N = dY.shape
     r = B.shape[1]
     _need(dY, torch.bfloat16, "dY")
     _need(B, torch.bfloat16, "B", (N, r))
     G = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=dY.device)
-    check(lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(B), r, float(scale), _ptr(G), _stream(dY)),
-          "qlora_lora_grad_in")
+    ws_bytes = lib().qlora_lora_grad_in_workspace_bytes(N, r)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dY.device)
+    if ws.numel() * ws.element_size() < ws_bytes:
+        raise ValueError("workspace smaller than %d bytes" % ws_bytes)
+    check(lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(B), r, float(scale), _ptr(G), _ptr(ws), ws_bytes,
+                                   _stream(dY)), "qlora_lora_grad_in")
     return G
 
 

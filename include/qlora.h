@@ -192,22 +192,32 @@ int qlora_nf4_matmul_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W
                          const uint16_t *T, const uint16_t *B, int32_t r, uint16_t *Y,
                          void *stream);
 
-/* G [M, r] = scale dY [M, N] B, B [N, r] (scale applied before rounding). */
+/* Workspace bytes for qlora_lora_grad_in: at least 256 for a supported
+ * shape, 0 if the shape is unsupported. */
+size_t qlora_lora_grad_in_workspace_bytes(int64_t N, int32_t r);
+
+/* G [M, r] = scale dY [M, N] B, B [N, r] (scale applied before rounding).
+ * B is read transposed straight from its [N, r] layout; the workspace only
+ * holds a zero-padded copy of B when r % 8 != 0.  ws: device memory of
+ * qlora_lora_grad_in_workspace_bytes(N, r) bytes, 16-byte aligned.  Requires
+ * N % 8 == 0, 1 <= r <= 128. */
 int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r,
-                       float scale, uint16_t *G, void *stream);
+                       float scale, uint16_t *G, void *ws, size_t ws_bytes, void *stream);
 
 /* dX [M, K] = dY deq(W) + G A with G = scale dY B [M, r] given.  No workspace. */
 int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W,
                         const uint16_t *G, const uint16_t *A, int32_t r, uint16_t *dX,
                         void *stream);
 
-/* Workspace bytes for qlora_lora_grads. */
+/* Workspace bytes for qlora_lora_grads (at least 256; 0 if unsupported). */
 size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 
 /* dA [r, K] = G^T X and/or dB [N, r] = dY^T T, with G = scale dY B and
- * T = scale X A^T as produced above (either output may be NULL), reduced
- * over M in fp32 split-M partials plus a fixed-order second pass.  G and X
- * are needed for dA, dY and T for dB. */
+ * T = scale X A^T as produced above (either output may be NULL).  The
+ * contraction runs over M: when the d-tiles alone do not fill the GPU, M is
+ * split and the fp32 split partials (in the workspace) are summed in split
+ * order by a second pass (deterministic).  G and X are needed for dA (K % 8
+ * == 0), dY and T for dB (N % 8 == 0). */
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
                      const uint16_t *T, int64_t M, int64_t N, int64_t K, int32_t r,
                      uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream);

@@ -100,9 +100,15 @@ def test_validation_rejects_before_launch():
     assert L.qlora_lora_down(P, 0, 64, P, 8, 1.0, P, None) == OK
     assert L.qlora_lora_down(P, 4, 60, P, 8, 1.0, P, None) == SHAPE
     assert L.qlora_lora_down(P, 4, 64, P, 8, float("inf"), P, None) == INVALID
-    assert L.qlora_lora_grad_in(P, 4, 60, P, 200, 1.0, P, None) == SHAPE
+    assert L.qlora_lora_grad_in(P, 4, 60, P, 200, 1.0, P, P, 1 << 20, None) == SHAPE
+    assert L.qlora_lora_grad_in(P, 4, 64, P, 8, 1.0, P, None, 0, None) == WS
+    assert L.qlora_lora_grad_in_workspace_bytes(11008, 64) == 256
+    assert L.qlora_lora_grad_in_workspace_bytes(11008, 65) >= 11008 * 72 * 2
+    assert L.qlora_lora_grad_in_workspace_bytes(11001, 64) == 0
     assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 8, P, P, None, 0, None) == WS
     assert L.qlora_lora_grads(P, P, P, P, 4, 64, 64, 0, P, P, P, 1 << 30, None) == SHAPE
+    assert L.qlora_lora_grads(P, P, P, P, 4, 60, 64, 8, None, P, P, 1 << 30, None) == SHAPE   # dB needs N % 8
+    assert L.qlora_lora_grads(P, P, P, P, 4, 64, 60, 8, P, None, P, 1 << 30, None) == SHAPE   # dA needs K % 8
     # grouped forward: bad count, bad descriptor, workspace
     D = _capi.LinearDescStruct
     ok = D(0x20000, ctypes.pointer(w), 0x20000, 0x20000, 8, 1.0, 0x20000, 0)
