@@ -10,24 +10,32 @@
 // "QLoRA: Efficient Finetuning of Quantized LLMs", Deep Analysis /
 // Methodology: the backward matmul dequantizes to 16-bit):
 //     dX [M, K] = [dY | G] [deq(W) ; A],           G = s dY B (given)
-// contraction over N: the dequantized tile is written transposed into LDS.
+// contraction over N.
 //
 // Design (both kernels):
-//  * 256 x 256 output tile, contraction step 64, 512 threads = 8 waves in two
-//    groups of 4.  Group g owns output rows 128 g .. +127; wave (g, q) owns a
-//    128 x 64 block computed with 4 x 2 MFMA 32x32x16 bf16 (fp32 accumulate).
-//  * Ping-pong: each step has two phases separated by barriers.  In phase 0
-//    group 0 runs its MFMAs on stage `cur` while group 1 dequantizes its half
-//    of the next weight tile into stage `cur ^ 1`; in phase 1 the roles swap.
-//    One wave per SIMD issues MFMAs while the other does the VALU/LDS work of
-//    the dequantization, so the matrix cores never wait for the expansion.
+//  * 256 x 256 output tile, contraction step 64, 512 threads = 8 waves, two
+//    per SIMD.  Wave (wm, wn) owns the 128 x 64 block (rows 128 wm, columns
+//    64 wn) as 4 x 2 MFMA 32x32x16 bf16 accumulators (fp32).
+//  * Every wave multiplies and dequantizes: during step t it runs the 32
+//    MFMAs of stage t while its threads expand the weight tile of step t + 1
+//    into the other stage (each thread half a 64-code block: one absmax
+//    constant, 32 table lookups, 4 16-byte LDS writes).  The two waves of a
+//    SIMD overlap one's expansion with the other's MFMAs.  One barrier per
+//    step.
+//  * Expansion: each of the 16 fp32 NF4 levels sits in its own LDS bank, so the
+//    64 lanes' lookups never conflict; each weight is fl32(level * c_hat)
+//    rounded to bf16, as in the dequantizer.
 //  * The left operand (X or dY) goes global -> LDS with 16-byte DMA loads
-//    (global_load_lds_dwordx4), rows XOR-swizzled by 16-byte chunk so that
-//    both the DMA writes and the MFMA operand reads are bank-conflict free.
-//    The two stages are separate LDS arrays so the compiler does not wait for
-//    the DMA before reading the other stage.
-//  * Packed weight bytes, block codes and group scales are prefetched two
-//    steps ahead in registers.
+//    (global_load_lds_dwordx4) one step ahead; packed weight bytes, block codes
+//    and group scales are prefetched two steps ahead in registers.
+//  * LDS tiles are 16-byte-chunk XOR-swizzled by row so that DMA writes,
+//    expansion writes and MFMA operand reads are bank-conflict free.  The
+//    forward weight tile is [256 n][64 k] (read like the left operand); the
+//    dX tile is [64 n][256 k], written row-wise by the expansion and read
+//    column-wise with ds_read_b64_tr_b16 (within a group of 16 lanes, lane i
+//    gets element i % 4 of the 8-byte reads of lanes i / 4 + 4 e, e = 0..3),
+//    which yields the 8-consecutive-n operands without a transposed store.
+//  * Operands of MFMA sub-step s + 1 are read while sub-step s multiplies.
 //  * Tiles are mapped so that consecutive tiles (sharing left-operand rows)
 //    run on the same XCD and its L2.
 //  * Epilogue: accumulators -> bf16 (round to nearest even) -> per-wave LDS
@@ -44,72 +52,35 @@ namespace qlora {
 __constant__ uint32_t cMMNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
 __constant__ uint32_t cMMT8Level[256] = {QLORA_T8_LEVEL_BITS};
 
-constexpr int kBM = 256;               // output rows per tile
-constexpr int kBN = 256;               // output columns per tile
-constexpr int kBK = 64;                // contraction step
+namespace {
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 256;                  // output rows per tile
+constexpr int kBN = 256;                  // output columns per tile
+constexpr int kBK = 64;                   // contraction step
 constexpr int kThreadsMM = 512;
-constexpr int kXBytes = kBM * kBK * 2;         // left stage: 256 rows x 128 B (swizzled)
-constexpr int kWLd = kBK + 8;                  // right stage row stride in bf16 (144 B, padded)
-constexpr int kWBytes = kBN * kWLd * 2;        // right stage bytes
+constexpr int kStageBytes = 256 * 64 * 2; // every stage holds 256 x 64 bf16
+constexpr int kBlockLoads = 3;            // VMEM loads per thread for half a weight block
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8; a field at its maximum does not wait).
-constexpr int kWaitLgkm0 = 0xC07F;          // lgkmcnt(0)
-constexpr int kWaitVm0Lgkm0 = 0x0070;       // vmcnt(0) lgkmcnt(0)
-constexpr int kWaitVm3Lgkm0 = 0x0073;       // all but the 3 refill loads of a forward step
-constexpr int kWaitVm6Lgkm0 = 0x0076;       // all but the 6 refill loads of a dX step
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8); vm = 63 / lgkm = 15 do not wait.
+constexpr int wait_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | 0x70 | ((lgkm & 15) << 8); }
 
-// Wave roles.  The two wave groups must share every SIMD (one wave of each per
-// SIMD) so that one group's MFMAs overlap the other group's expansion; waves of
-// a workgroup are placed on the 4 SIMDs round-robin (wave w on SIMD w % 4), so
-// waves 0-3 form group 0 and waves 4-7 group 1.
-#ifndef QLORA_GROUP_OF_WAVE
-#define QLORA_GROUP_OF_WAVE(w) ((w) >> 2)
-#define QLORA_INDEX_IN_GROUP(w) ((w) & 3)
-#endif
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
-__device__ __forceinline__ int wave_group() { return QLORA_GROUP_OF_WAVE(wave_id()); }
-__device__ __forceinline__ int wave_in_group() { return QLORA_INDEX_IN_GROUP(wave_id()); }
-// thread index 0..255 within its group
-__device__ __forceinline__ int thread_in_group() { return wave_in_group() * 64 + (threadIdx.x & 63); }
-
-// Byte offset of 16-byte chunk `chunk` (0..7) of row `row` in a swizzled stage.
-__device__ __forceinline__ int xswz(int row, int chunk) {
+// 128-byte rows (64 bf16): chunk c of row r at 16-byte position c ^ f(r).
+__device__ __forceinline__ int swz128(int row, int chunk) {
   return row * 128 + 16 * (chunk ^ ((row & 7) ^ ((row >> 3) & 1)));
 }
-
-// Left operand tile: rows m0 .. m0+255 of a row-major bf16 matrix (row
-// stride ld elements, `cols` columns, cols % 8 == 0), columns c0 .. c0+63,
-// DMA'd into a swizzled stage by the 4 waves of one group (`gw` = wave index
-// within the group).  Each wave issues blocks u = 8 gw .. 8 gw + 7 of 8 rows
-// (1 KB, one DMA instruction each); lane i of a block lands in slot i, i.e.
-// row 8 u + i / 8 at position i % 8, which holds logical chunk
-// (i % 8) ^ swizzle(row).  Rows past `rows` are clamped to the last row
-// (their results are never stored); chunks past `cols` are clamped to the
-// row's last chunk (finite data that meets zero weights in the contraction
-// tail).
-__device__ __forceinline__ void dma_left(uint8_t *stage, const uint16_t *src, int64_t ld, int m0, int rows,
-                                         int c0, int cols, int gw) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int u = gw * 8 + j;
-    const int row = u * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
-    const int grow = min(m0 + row, rows - 1);
-    const int gcol = min(c0 + chunk * 8, cols - 8);
-    const uint16_t *g = src + static_cast<int64_t>(grow) * ld + gcol;
-    const int off = __builtin_amdgcn_readfirstlane(u * 1024);
-    __builtin_amdgcn_global_load_lds(g, QLORA_LDS(stage + off), 16, 0, 0);
-  }
+// 512-byte rows (256 bf16): chunk c (0..31) of row r at c ^ g(r),
+// g(r) = 4 (r % 4) + (r / 4) % 4 (within the chunk's half row).
+__device__ __forceinline__ int swz512(int row, int chunk) {
+  return row * 512 + 16 * (chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)));
 }
 
-// Workgroup barrier without a memory-model fence: waits for this wave's LDS
-// operations (and, with kWaitVm*, for its DMA loads) and then s_barrier.  A
-// fence would also wait for every outstanding DMA and prefetch load.  The
-// signal fences stop the compiler from moving memory accesses across it, and
-// the scheduling barriers keep each phase its own scheduling region (no
-// instruction of one phase is moved into another).
+// Workgroup barrier without a memory-model fence (a fence would also wait for
+// every outstanding DMA and prefetch): waits per kWait, then s_barrier.  The
+// signal fences stop the compiler from moving memory accesses across it and
+// the scheduling barriers keep each side its own scheduling region.
 template <int kWait>
 __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -120,86 +91,179 @@ __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One 64-wide contraction step of this wave's 128 x 64 block.
-// MFMA 32x32x16: lane l supplies row (l & 31) of A and column (l & 31) of B,
-// with contraction elements 8 (l >> 5) .. +7 of each 16-wide sub-step.
-__device__ __forceinline__ void mfma_step(const uint8_t *xs, const uint8_t *ws, f32x16_t (&acc)[4][2]) {
-  const int lane = threadIdx.x & 63;
-  const int wm = wave_group(), wn = wave_in_group();
-  const int lr = lane & 31, lh = lane >> 5;
+// Left operand tile: rows m0 .. m0+255 (clamped to rows - 1: never stored)
+// and columns c0 .. c0+63 (16-byte chunks clamped to the row's last chunk,
+// cols % 8 == 0: finite data that meets zero weights in a contraction tail)
+// of a row-major bf16 matrix with row pitch ld, DMA'd into a swizzled stage.
+// Wave w issues the four 1 KB instructions of rows 32 w .. 32 w + 31; lane i
+// of an instruction lands in slot i (row 8 u + i / 8, position i % 8).
+__device__ __forceinline__ void dma_left(uint8_t *stage, const uint16_t *src, int64_t ld, int m0, int rows, int c0,
+                                         int cols, int wave, int lane) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int chunk = 2 * s + lh;
-    bf16x8_t a[4], b[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t *>(xs + xswz(wm * 128 + 32 * i + lr, chunk));
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t *>(ws + (wn * 64 + 32 * j + lr) * (kWLd * 2) + chunk * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int j = 0; j < 4; ++j) {
+    const int u = wave * 4 + j;
+    const int row = u * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
+    const int grow = min(m0 + row, rows - 1);
+    const int gcol = min(c0 + chunk * 8, cols - 8);
+    const int off = __builtin_amdgcn_readfirstlane(u * 1024);
+    __builtin_amdgcn_global_load_lds(src + static_cast<int64_t>(grow) * ld + gcol, QLORA_LDS(stage + off), 16, 0,
+                                     0);
   }
 }
 
-// Narrow [rows, r] bf16 matrix (T, G or B) as one 64-wide contraction step:
-// columns j0 .. j0+63, zero past r.  Stored swizzled (left) or padded (right).
-template <bool kLeft>
+// Half of a 64-code weight block: 32 packed nibbles (low nibble first), the
+// block's first-level constant code and its group's second-level scale.
+struct WBlock {
+  uint4 p;
+  uint32_t code;
+  float c2;
+};
+
+// Codes 32 half .. +31 of the block W[n][k .. k+63] (n < N, k % 64 == 0, k < K).
+__device__ __forceinline__ void load_block(WBlock &b, const NF4View &w, int n, int k, int half) {
+  const int64_t blk = (static_cast<int64_t>(n) * w.K + k) >> 6;
+  b.p = *reinterpret_cast<const uint4 *>(w.packed + (blk << 5) + 16 * half);
+  b.code = w.code8[blk];
+  b.c2 = w.c2[blk >> 8];
+}
+
+// NF4 level lookups from the 16-entry fp32 table: for a packed word w (8
+// codes) lo4 / hi4 hold 4 x (low / high) nibble of every byte, i.e. the byte
+// offsets of the levels of codes 2 b and 2 b + 1.
+__device__ __forceinline__ uint32_t nf4_lo4(uint32_t w) { return (w << 2) & 0x3C3C3C3Cu; }
+__device__ __forceinline__ uint32_t nf4_hi4(uint32_t w) { return (w >> 2) & 0x3C3C3C3Cu; }
+__device__ __forceinline__ float nf4_level(const float *nf4, uint32_t off4, int b) {
+  return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(nf4) + ((off4 >> (8 * b)) & 0xffu));
+}
+
+// Chunk c (codes 8 c .. 8 c + 7 of the half block) as 8 bf16 = fl32(level * chat).
+__device__ __forceinline__ uint4 expand_chunk(const WBlock &b, int c, float chat, const float *nf4) {
+  const uint32_t words[4] = {b.p.x, b.p.y, b.p.z, b.p.w};
+  const uint32_t lo4 = nf4_lo4(words[c]), hi4 = nf4_hi4(words[c]);
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(nf4_level(nf4, lo4, q) * chat, nf4_level(nf4, hi4, q) * chat);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ bf16x4_t ds_tr16(const uint8_t *p) {
+  typedef __attribute__((address_space(3))) bf16x4_t lds_t;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t *)((__attribute__((address_space(3))) uint8_t *)(p)));
+}
+
+// MFMA operands of one 16-wide sub-step: lane l supplies rows 32 i + l % 32
+// of the wave's left block and columns 32 j + l % 32 of its right block, with
+// contraction elements 8 (l / 32) .. +7 of the sub-step.
+struct Frag {
+  bf16x8_t a[4], b[2];
+};
+
+// Per-thread byte offsets of the operand reads (fixed for the whole kernel):
+//   xo[s]     left block, sub-step s; fragment i adds 4096 i (32 rows), since
+//             the row swizzle repeats every 16 rows;
+//   wo[s]     forward weight block, likewise;
+//   to[j][h]  dX weight tile (transposed reads), half h of fragment j;
+//             sub-step s adds 8192 s (16 rows), the swizzle repeating every 16.
+struct OpOffsets {
+  uint32_t xo[4], wo[4], to[2][2];
+};
+
+template <bool kDx>
+__device__ __forceinline__ OpOffsets op_offsets() {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 31, lh = lane >> 5;
+  OpOffsets o;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    o.xo[s] = static_cast<uint32_t>(swz128(128 * wm + lr, 2 * s + lh));
+    o.wo[s] = static_cast<uint32_t>(swz128(64 * wn + lr, 2 * s + lh));
+  }
+  // [64 n][256 k] tile: group G = lane / 16 reads columns
+  // 64 wn + 32 j + 16 (G % 2) .. +15, rows 8 (G / 2) + 4 h .. +3 (+ 16 s);
+  // source lane t points at row t / 4, columns 4 (t % 4) .. +3.
+  const int t = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      o.to[j][h] = static_cast<uint32_t>(
+          swz512(8 * (g >> 1) + 4 * h + (t >> 2), 8 * wn + 4 * j + 2 * (g & 1) + ((t & 3) >> 1)) + 8 * (t & 1));
+  return o;
+}
+
+template <bool kDx>
+__device__ __forceinline__ void load_frag(Frag &f, const uint8_t *xs, const uint8_t *ws, const OpOffsets &o, int s) {
+  // in the order the MFMAs (i major, j minor) first need them: a0 b0 b1 a1 a2 a3
+  auto ld_a = [&](int i) { f.a[i] = *reinterpret_cast<const bf16x8_t *>(xs + o.xo[s] + 4096 * i); };
+  auto ld_b = [&](int j) {
+    if (!kDx) {
+      f.b[j] = *reinterpret_cast<const bf16x8_t *>(ws + o.wo[s] + 4096 * j);
+    } else {
+      const bf16x4_t lo = ds_tr16(ws + o.to[j][0] + 8192 * s);
+      const bf16x4_t hi = ds_tr16(ws + o.to[j][1] + 8192 * s);
+      f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  ld_a(0);
+  ld_b(0);
+  ld_b(1);
+  ld_a(1);
+  ld_a(2);
+  ld_a(3);
+}
+
+__device__ __forceinline__ void mfma_frag(const Frag &f, f32x16_t (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// A whole 64-wide step without expansion (the LoRA steps).
+template <bool kDx>
+__device__ __forceinline__ void mfma_stage(const uint8_t *xs, const uint8_t *ws, const OpOffsets &o,
+                                           f32x16_t (&acc)[4][2]) {
+  Frag f[2];
+  load_frag<kDx>(f[0], xs, ws, o, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < 3) load_frag<kDx>(f[(s + 1) & 1], xs, ws, o, s + 1);
+    mfma_frag(f[s & 1], acc);
+  }
+}
+
+// Narrow [rows, r] bf16 matrix (T, G or B), columns j0 .. j0+63 (zero past r)
+// of rows row0 .. row0+255 (zero past `rows`), into a 128-byte-row stage.
 __device__ __forceinline__ void load_narrow(uint8_t *stage, const uint16_t *src, int r, int row0, int rows, int j0) {
   if ((r & 7) == 0) {
-    for (int idx = threadIdx.x; idx < kBM * 8; idx += kThreadsMM) {
+    for (int idx = threadIdx.x; idx < 256 * 8; idx += kThreadsMM) {
       const int row = idx >> 3, c = idx & 7;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (row0 + row < rows && j0 + 8 * c < r)
         v = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(row0 + row) * r + j0 + 8 * c);
-      const int off = kLeft ? xswz(row, c) : row * (kWLd * 2) + 16 * c;
-      *reinterpret_cast<uint4 *>(stage + off) = v;
+      *reinterpret_cast<uint4 *>(stage + swz128(row, c)) = v;
     }
   } else {
-    for (int idx = threadIdx.x; idx < kBM * 64; idx += kThreadsMM) {
+    for (int idx = threadIdx.x; idx < 256 * 64; idx += kThreadsMM) {
       const int row = idx >> 6, j = idx & 63;
       uint16_t v = 0;
       if (row0 + row < rows && j0 + j < r) v = src[static_cast<int64_t>(row0 + row) * r + j0 + j];
-      const int off = kLeft ? xswz(row, j >> 3) + 2 * (j & 7) : row * (kWLd * 2) + 2 * j;
-      *reinterpret_cast<uint16_t *>(stage + off) = v;
+      *reinterpret_cast<uint16_t *>(stage + swz128(row, j >> 3) + 2 * (j & 7)) = v;
     }
   }
 }
 
-// Epilogue: each wave writes its 128 x 64 block as bf16 into its own 16 KB LDS
-// region (16-byte chunks XOR-swizzled by row), then streams it out with
-// 16-byte stores guarded by the matrix bounds (ncols % 8 == 0).
-// MFMA 32x32 output layout: lane l holds column l & 31; element e holds row
-// 8 (e / 4) + 4 (l >> 5) + (e % 4).
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][2], uint8_t *region, uint16_t *out, int64_t ld,
-                                           int row0, int col0, int nrows, int ncols) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int c = 32 * j + (lane & 31);
-        const int off = r * 128 + 16 * ((c >> 3) ^ (r & 7)) + 2 * (c & 7);
-        *reinterpret_cast<uint16_t *>(region + off) = f32_to_bf16(acc[i][j][e]);
-      }
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int idx = t * 64 + lane;
-    const int r = idx >> 3, c = idx & 7;
-    const uint4 v = *reinterpret_cast<const uint4 *>(region + r * 128 + 16 * (c ^ (r & 7)));
-    const int gr = row0 + r, gc = col0 + 8 * c;
-    if (gr < nrows && gc < ncols) *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(gr) * ld + gc) = v;
-  }
-}
-
-__device__ __forceinline__ void init_tables(float2 *lut2, float *t8) {
-  for (int i = threadIdx.x; i < 256; i += kThreadsMM) {
-    lut2[i] = make_float2(u2f(cMMNF4Level[i & 15]), u2f(cMMNF4Level[i >> 4]));
-    t8[i] = u2f(cMMT8Level[i]);
+// A [r, K] rows j0 .. j0+63 (zero past r) and columns k0 .. k0+255 (zero past
+// K) into a [64 j][256 k] stage (the dX weight layout).
+__device__ __forceinline__ void load_a_tile(uint8_t *stage, const uint16_t *A, int r, int K, int j0, int k0) {
+  for (int idx = threadIdx.x; idx < 64 * 32; idx += kThreadsMM) {
+    const int j = idx >> 5, c = idx & 31;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (j0 + j < r && k0 + 8 * c < K)
+      v = *reinterpret_cast<const uint4 *>(A + static_cast<int64_t>(j0 + j) * K + k0 + 8 * c);
+    *reinterpret_cast<uint4 *>(stage + swz512(j, c)) = v;
   }
 }
 
@@ -214,263 +278,168 @@ __device__ __forceinline__ void tile_coords(int tiles_cols, int &tr, int &tc) {
   tc = lid % tiles_cols;
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][2]) {
+}  // namespace
+
+// kDx = false: left = X [M, K] (contraction K), weight tile [256 n][64 k].
+// kDx = true:  left = dY [M, N] (contraction N), weight tile [64 n][256 k].
+template <bool kDx>
+__global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restrict__ L, int M, NF4View w,
+                                                       const uint16_t *__restrict__ Ln,
+                                                       const uint16_t *__restrict__ Rn, int r,
+                                                       uint16_t *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t sX0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sX1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sW0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sW1[kStageBytes];
+  __shared__ __attribute__((aligned(64))) float sNf4[16];
+  __shared__ float sT8[256];
+
+  const int K = w.K, N = w.N;
+  const int ncols = kDx ? K : N;           // output columns
+  const int Kc = kDx ? N : K;              // contraction length (multiple of 8; of 64 for the forward)
+  int tr, tc;
+  tile_coords((ncols + kBN - 1) / kBN, tr, tc);
+  const int m0 = tr * kBM, c0 = tc * kBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float mean = w.mean[0];
+  const int KT = (Kc + kBK - 1) / kBK;
+
+  // This thread's half block in contraction step kt (half = tid % 2):
+  //   forward: row n = c0 + tid / 2 (an output column), k = 64 kt
+  //   dX:      row n = 64 kt + tid / 8 (a contraction index),
+  //            k = c0 + 64 ((tid / 2) % 4)
+  // Neighbouring lanes read neighbouring bytes of a row (the two halves of a
+  // block; in dX the 8 lanes of a row cover its 4 blocks, one 128-byte line),
+  // so a load instruction touches few cache lines.  Rows past N (dX
+  // contraction tail) expand to exact zeros; columns past the matrix are
+  // clamped (never stored).
+  const int half = tid & 1;
+  const int trow = kDx ? (tid >> 3) : (tid >> 1);     // row of the tile
+  const int tkb = kDx ? ((tid >> 1) & 3) : 0;         // block within the tile row (dX)
+  auto block_load = [&](WBlock &b, int kt) __attribute__((always_inline)) {
+    if (kDx)
+      load_block(b, w, min(kBK * kt + trow, N - 1), min(c0 + 64 * tkb, K - 64), half);
+    else
+      load_block(b, w, min(c0 + trow, N - 1), kBK * kt, half);
+  };
+  auto block_chat = [&](const WBlock &b, int kt) __attribute__((always_inline)) {
+    const float c = decode_absmax(sT8[b.code], b.c2, mean);
+    return (kDx && kBK * kt + trow >= N) ? 0.f : c;
+  };
+  auto put_chunk = [&](uint8_t *ws, int c, uint4 v) __attribute__((always_inline)) {
+    if (kDx)
+      *reinterpret_cast<uint4 *>(ws + swz512(trow, 8 * tkb + 4 * half + c)) = v;
+    else
+      *reinterpret_cast<uint4 *>(ws + swz128(trow, 4 * half + c)) = v;
+  };
+
+  const OpOffsets ops = op_offsets<kDx>();
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-}
 
-// ===========================================================================
-// Forward
-// ===========================================================================
-
-// Packed weight bytes of one thread's share of a tile: group g expands weight
-// rows 128 g .. +127 of the tile; thread (tg = tid % 256) takes row tg / 2 and
-// 32 codes (16 bytes) of half tg % 2 of the row's 64-element block.
-struct FwdPack {
-  uint4 p;
-  uint32_t code;
-  float c2;
-  __device__ __forceinline__ void load(const NF4View &w, int n0, int k0) {
-    const int tg = thread_in_group(), grp = wave_group();
-    const int n = min(n0 + 128 * grp + (tg >> 1), w.N - 1);
-    const int64_t blk = (static_cast<int64_t>(n) * w.K + k0) >> 6;
-    p = *reinterpret_cast<const uint4 *>(w.packed + (blk << 5) + (tg & 1) * 16);
-    code = w.code8[blk];
-    c2 = w.c2[blk >> 8];
+  for (int i = tid; i < 256; i += kThreadsMM) {
+    if (i < 16) sNf4[i] = u2f(cMMNF4Level[i]);
+    sT8[i] = u2f(cMMT8Level[i]);
   }
-  __device__ __forceinline__ void expand(uint8_t *ws, const float2 *lut2, const float *t8, float mean) const {
-    const int tg = thread_in_group(), grp = wave_group();
-    const int row = 128 * grp + (tg >> 1), half = tg & 1;
-    const float chat = decode_absmax(t8[code], c2, mean);
-    const uint32_t words[4] = {p.x, p.y, p.z, p.w};
-    uint32_t o[16];
+
+  // Prologue: block of step 0 expanded into stage 0, left tile 0 DMA'd, the
+  // block of step 1 in flight.
+  WBlock b0, b1;
+  block_load(b0, 0);
+  block_load(b1, min(1, KT - 1));
+  dma_left(sX0, L, Kc, m0, M, 0, Kc, wave, lane);
+  __syncthreads();   // tables
+  {
+    const float chat = block_chat(b0, 0);
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float2 l = lut2[(words[wd] >> (8 * b)) & 0xffu];
-        o[wd * 4 + b] = pack_bf16x2(l.x * chat, l.y * chat);
-      }
-    uint4 *d = reinterpret_cast<uint4 *>(ws + row * (kWLd * 2) + half * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    for (int c = 0; c < 4; ++c) put_chunk(sW0, c, expand_chunk(b0, c, chat, sNf4));
   }
-};
+  raw_barrier<wait_imm(kBlockLoads, 0)>();
 
-// ===========================================================================
-// dX
-// ===========================================================================
-
-// Group g expands tile columns (K) 128 g .. +127 for all 64 contraction rows
-// (N).  Thread tg: weight rows 2 (tg % 32), +1 and 16 columns 16 (tg / 32) ..
-// +15 (8 packed bytes per row, one block constant per row).  Written
-// transposed: LDS row = K column, two adjacent N values per 32-bit word.
-struct DxPack {
-  uint2 p0, p1;
-  uint32_t code0, code1;
-  float c20, c21;
-  __device__ __forceinline__ void load(const NF4View &w, int n0, int k0) {
-    const int tg = thread_in_group(), grp = wave_group();
-    const int n = n0 + 2 * (tg & 31);
-    const int na = min(n, w.N - 1), nb = min(n + 1, w.N - 1);
-    const int k = min(k0 + 128 * grp + 16 * (tg >> 5), w.K - 16);
-    const int64_t e0 = static_cast<int64_t>(na) * w.K + k, e1 = static_cast<int64_t>(nb) * w.K + k;
-    p0 = *reinterpret_cast<const uint2 *>(w.packed + (e0 >> 1));
-    p1 = *reinterpret_cast<const uint2 *>(w.packed + (e1 >> 1));
-    code0 = w.code8[e0 >> 6];
-    code1 = w.code8[e1 >> 6];
-    c20 = w.c2[e0 >> 14];
-    c21 = w.c2[e1 >> 14];
-  }
-  // Rows past N must contribute zero: they multiply dY columns that are zero
-  // only if the weight rows are zero too (dY past N is never loaded as data).
-  __device__ __forceinline__ void expand(uint8_t *ws, const float2 *lut2, const float *t8, float mean, int n0,
-                                         int N) const {
-    const int tg = thread_in_group(), grp = wave_group();
-    const int np = tg & 31;
-    const int kl = 128 * grp + 16 * (tg >> 5);
-    const float ch0 = (n0 + 2 * np < N) ? decode_absmax(t8[code0], c20, mean) : 0.f;
-    const float ch1 = (n0 + 2 * np + 1 < N) ? decode_absmax(t8[code1], c21, mean) : 0.f;
-    const uint32_t w0[2] = {p0.x, p0.y}, w1[2] = {p1.x, p1.y};
-#pragma unroll
-    for (int wd = 0; wd < 2; ++wd)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float2 la = lut2[(w0[wd] >> (8 * b)) & 0xffu];
-        const float2 lb = lut2[(w1[wd] >> (8 * b)) & 0xffu];
-        const uint32_t pa = pack_bf16x2(la.x * ch0, la.y * ch0);   // row n:   k, k+1
-        const uint32_t pb = pack_bf16x2(lb.x * ch1, lb.y * ch1);   // row n+1: k, k+1
-        const int k = kl + wd * 8 + b * 2;
-        *reinterpret_cast<uint32_t *>(ws + k * (kWLd * 2) + 4 * np) = __builtin_amdgcn_perm(pb, pa, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(ws + (k + 1) * (kWLd * 2) + 4 * np) =
-            __builtin_amdgcn_perm(pb, pa, 0x07060302u);
-      }
-  }
-};
-
-// A [r, K] rows j0 .. j0+63 (zero past r), columns k0 .. k0+255, transposed
-// into a padded right stage as [k][j].
-__device__ __forceinline__ void load_a_transposed(uint8_t *ws, const uint16_t *A, int r, int K, int j0, int k0) {
-  for (int idx = threadIdx.x; idx < kBK * kBN; idx += kThreadsMM) {
-    const int j = idx >> 8, k = idx & 255;
-    uint16_t v = 0;
-    if (j0 + j < r && k0 + k < K) v = A[static_cast<int64_t>(j0 + j) * K + k0 + k];
-    *reinterpret_cast<uint16_t *>(ws + k * (kWLd * 2) + 2 * j) = v;
-  }
-}
-
-// ===========================================================================
-// The ping-pong main loop, shared by both kernels.
-//   kDx = false: left = X [M, K] (contraction K), right = deq(W) rows.
-//   kDx = true:  left = dY [M, N] (contraction N), right = deq(W)^T.
-// ===========================================================================
-template <bool kDx>
-struct Pack;
-template <>
-struct Pack<false> {
-  using T = FwdPack;
-};
-template <>
-struct Pack<true> {
-  using T = DxPack;
-};
-
-template <bool kDx>
-__global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restrict__ L, int M, NF4View w,
-                                                       const uint16_t *__restrict__ Ln,
-                                                       const uint16_t *__restrict__ Rn, int r,
-                                                       uint16_t *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX0[kXBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sX1[kXBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sW0[kWBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sW1[kWBytes];
-  __shared__ float2 sLut[256];
-  __shared__ float sT8[256];
-  using P = typename Pack<kDx>::T;
-
-  const int K = w.K, N = w.N;
-  const int ncols = kDx ? K : N;           // output columns
-  const int Kc = kDx ? N : K;              // contraction length (multiple of 8; of 64 for the forward)
-  const int ldl = kDx ? N : K;             // row stride of the left operand
-  int tr, tc;
-  tile_coords((ncols + kBN - 1) / kBN, tr, tc);
-  const int m0 = tr * kBM, c0 = tc * kBN;
-  // wave-uniform group index in an SGPR, so the group branches are scalar
-  const int grp = __builtin_amdgcn_readfirstlane(wave_group());
-  const float mean = w.mean[0];
-  const int KT = (Kc + kBK - 1) / kBK;
-
-  // right-operand tile origin: forward (n0 = c0, k = step), dX (n = step, k0 = c0)
-  auto pack_load = [&](P &pk, int kt) {
-    if (kDx)
-      pk.load(w, kt * kBK, c0);
-    else
-      pk.load(w, c0, kt * kBK);
-  };
-  auto pack_expand = [&](const P &pk, uint8_t *ws, int kt) {
-    if constexpr (kDx)
-      pk.expand(ws, sLut, sT8, mean, kt * kBK, N);
-    else
-      pk.expand(ws, sLut, sT8, mean);
-  };
-  // In a contraction tail (dX with N % 64 != 0) the DMA cannot zero the dY
-  // columns past N; their chunks are clamped to valid data and the weight rows
-  // past N are expanded as exact zeros, so they contribute nothing.
-  const int gw = __builtin_amdgcn_readfirstlane(wave_in_group());
-
-  f32x16_t acc[4][2];
-  zero_acc(acc);
-  init_tables(sLut, sT8);
-
-  P pk0, pk1;
-  pack_load(pk0, 0);
-  if (KT > 1) pack_load(pk1, 1);
-  if (grp == 1) dma_left(sX0, L, ldl, m0, M, 0, Kc, gw);
-  __syncthreads();                 // tables ready
-  pack_expand(pk0, sW0, 0);
-  if (KT > 2) pack_load(pk0, 2);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
-  __syncthreads();
-
-  // Pipeline steps: multiply stage CUR, fill stage CUR ^ 1 with step kt + 1.
-  // Group 1 expands its half of the next weight tile in phase 0, then issues
-  // the DMA of the next left tile and its refill loads; group 0 expands its
-  // half in phase 1.  The DMA has a whole phase (the other group's MFMAs) to
-  // land before the end-of-step barrier.  Each group runs its own loop (the
-  // barrier sequence is identical), so no register state merges across groups.
-  // Refill loads always go out (clamped to the last step) to keep the register
-  // flow branch-free; the extra loads near the end are never used.
-  constexpr int kEndWait = kDx ? kWaitVm6Lgkm0 : kWaitVm3Lgkm0;
-  // `more` (a next step exists) is a compile-time flag: the unrolled loop body
-  // is branch-free, so the compiler's load-wait bookkeeping stays exact and it
-  // never drains the prefetches it does not need.
-  auto step0 = [&](auto cur_tag, auto more_tag, int kt, P &pk) __attribute__((always_inline)) {
+  // Step kt: DMA the left tile of kt + 1 into the other stage, then load the
+  // block of kt + 2 into the registers freed by step kt - 1 (these loads are
+  // the newest memory operations: the end-of-step wait lets them fly while
+  // the DMA must land); multiply stage CUR while expanding the block of kt + 1
+  // (loaded a step ago) into the other weight stage, one chunk per MFMA
+  // sub-step; wait for the DMA and the LDS writes; barrier.
+  auto step = [&](auto cur_tag, int kt, WBlock &bn, WBlock &bl) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_tag)::value;
-    constexpr bool kMore = decltype(more_tag)::value;
-    mfma_step(CUR ? sX1 : sX0, CUR ? sW1 : sW0, acc);
-    raw_barrier<kWaitLgkm0>();
-    if constexpr (kMore) {
-      pack_expand(pk, CUR ? sW0 : sW1, min(kt + 1, KT - 1));
-      pack_load(pk, min(kt + 3, KT - 1));
+    const uint8_t *xs = CUR ? sX1 : sX0;
+    const uint8_t *wr = CUR ? sW1 : sW0;
+    uint8_t *xn = CUR ? sX0 : sX1;
+    uint8_t *wn = CUR ? sW0 : sW1;
+    // First use of the block of kt + 1 before any newer load is issued: the
+    // wait for it then covers only loads issued a step ago.
+    const float chat = block_chat(bn, kt + 1);
+    asm volatile("" ::"v"(bn.p.x), "v"(bn.p.y), "v"(bn.p.z), "v"(bn.p.w), "v"(chat));
+    __builtin_amdgcn_sched_barrier(0);
+    dma_left(xn, L, Kc, m0, M, min(kt + 1, KT - 1) * kBK, Kc, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    block_load(bl, min(kt + 2, KT - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    Frag f[2];
+    load_frag<kDx>(f[0], xs, wr, ops, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) load_frag<kDx>(f[(s + 1) & 1], xs, wr, ops, s + 1);
+      put_chunk(wn, s, expand_chunk(bn, s, chat, sNf4));
+      mfma_frag(f[s & 1], acc);
     }
-    raw_barrier<kEndWait>();
-  };
-  auto step1 = [&](auto cur_tag, auto more_tag, int kt, P &pk) __attribute__((always_inline)) {
-    constexpr int CUR = decltype(cur_tag)::value;
-    constexpr bool kMore = decltype(more_tag)::value;
-    if constexpr (kMore) {
-      pack_expand(pk, CUR ? sW0 : sW1, min(kt + 1, KT - 1));
-      dma_left(CUR ? sX0 : sX1, L, ldl, m0, M, min(kt + 1, KT - 1) * kBK, Kc, gw);
-      // The end-of-step wait counts on the refill loads being the newest
-      // memory operations of this wave: nothing may move across this point.
-      __builtin_amdgcn_sched_barrier(0);
-      pack_load(pk, min(kt + 3, KT - 1));
-    }
-    raw_barrier<kWaitLgkm0>();
-    mfma_step(CUR ? sX1 : sX0, CUR ? sW1 : sW0, acc);
-    raw_barrier<kEndWait>();   // this group's DMA has landed
+    raw_barrier<wait_imm(kBlockLoads, 0)>();
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  // Every step of the loop prepares a next one (the step past the end expands
-  // and loads a clamped, never-used tile), so the loop body has no branches.
-  // An odd number of steps ends with one single step.
-  const int KT2 = KT & ~1;
-  if (grp == 0) {
-    for (int kt = 0; kt < KT2; kt += 2) {
-      step0(C0(), T_(), kt, pk1);
-      step0(C1(), T_(), kt + 1, pk0);
-    }
-    if (KT & 1) step0(C0(), F_(), KT - 1, pk1);
-  } else {
-    for (int kt = 0; kt < KT2; kt += 2) {
-      step1(C0(), T_(), kt, pk1);
-      step1(C1(), T_(), kt + 1, pk0);
-    }
-    if (KT & 1) step1(C0(), F_(), KT - 1, pk1);
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(C0(), kt, b1, b0);
+    step(C1(), kt + 1, b0, b1);
   }
+  if (kt < KT) step(C0(), kt, b1, b0);
 
-  // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A^T.
+  // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A [r, K].
   for (int j0 = 0; j0 < r; j0 += kBK) {
-    load_narrow<true>(sX0, Ln, r, m0, M, j0);
+    load_narrow(sX0, Ln, r, m0, M, j0);
     if (kDx)
-      load_a_transposed(sW0, Rn, r, K, j0, c0);
+      load_a_tile(sW0, Rn, r, K, j0, c0);
     else
-      load_narrow<false>(sW0, Rn, r, c0, N, j0);
+      load_narrow(sW0, Rn, r, c0, N, j0);
     __syncthreads();
-    mfma_step(sX0, sW0, acc);
+    mfma_stage<kDx>(sX0, sW0, ops, acc);
     __syncthreads();
   }
 
-  const int wave = wave_id();
+  // Epilogue: the wave's 128 x 64 block as bf16 into its own 16 KB region
+  // (16-byte chunks XOR-swizzled by row), then 16-byte stores guarded by the
+  // matrix bounds (ncols % 8 == 0).  MFMA 32x32 output layout: lane l holds
+  // column l % 32; element e holds row 8 (e / 4) + 4 (l / 32) + e % 4.
   uint8_t *region = (wave < 2 ? sX0 : wave < 4 ? sX1 : wave < 6 ? sW0 : sW1) + (wave & 1) * 16384;
-  store_tile(acc, region, out, ncols, m0 + wave_group() * 128, c0 + wave_in_group() * 64, M, ncols);
+  const int wm = wave >> 2, wnn = wave & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int cc = 32 * j + (lane & 31);
+        *reinterpret_cast<uint16_t *>(region + rr * 128 + 16 * ((cc >> 3) ^ (rr & 7)) + 2 * (cc & 7)) =
+            f32_to_bf16(acc[i][j][e]);
+      }
+  __builtin_amdgcn_s_waitcnt(wait_imm(63, 0));
+#pragma unroll 4
+  for (int t = 0; t < 16; ++t) {
+    const int idx = t * 64 + lane;
+    const int rr = idx >> 3, c = idx & 7;
+    const uint4 v = *reinterpret_cast<const uint4 *>(region + rr * 128 + 16 * (c ^ (rr & 7)));
+    const int gr = m0 + 128 * wm + rr, gc = c0 + 64 * wnn + 8 * c;
+    if (gr < M && gc < ncols) *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(gr) * ncols + gc) = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
