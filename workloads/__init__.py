@@ -139,3 +139,17 @@ def device_normal(shape, std: float, seed: int, device, dtype=None):
     t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     t.mul_(std)
     return t if dtype is None else t.to(dtype)
+
+
+def device_layer_weights(cfg: LayerConfig, layer: int, device):
+    """The frozen weights of one layer of a multi-layer config, drawn on the
+    device: one torch.Generator seeded 65000 + layer draws the layer's linears
+    in order (q, k, v, o, gate, up, down) as N(0, W_STD^2) fp32 [out, in].
+    Yields (linear, tensor); each tensor is a fresh allocation."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(65000 + layer)
+    for lin in cfg.linears:
+        t = torch.randn((lin.out_features, lin.in_features), generator=g, device=device, dtype=torch.float32)
+        t.mul_(W_STD)
+        yield lin, t
