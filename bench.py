@@ -272,6 +272,53 @@ def quantize_bench(q, torch, workloads, cfg, dev, reps=5):
                 note="includes workspace allocation by the Python binding")
 
 
+def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3):
+    """fwd + bwd of all linears of one layer of `cfg` at `tokens` tokens."""
+    layers = [Layer(q, torch, workloads, lin, tokens, cfg.rank, 1000 * cfg.index + 10 * i, dev)
+              for i, lin in enumerate(cfg.linears)]
+    flops = sum(L.flops for L in layers)
+    for _ in range(warmup):
+        run_step(q, torch, layers, cfg.scale)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run_step(q, torch, layers, cfg.scale)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del layers
+    torch.cuda.empty_cache()
+    return dict(tokens=tokens, ms_per_step=round(ms, 3), step_flops=flops,
+                TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1), frac_bf16_peak=round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4))
+
+
+def model_quantize_bench(q, torch, workloads, cfg, dev):
+    """Quantize every layer of a multi-layer config, weights drawn on the device
+    layer by layer (the draws are not timed)."""
+    ms = 0.0
+    params = 0
+    stored = 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for layer in range(cfg.layers):
+        Ws = [W for _, W in workloads.device_layer_weights(cfg, layer, dev)]
+        torch.cuda.synchronize()
+        e0.record()
+        ws = [q.NF4Weight.quantize(W) for W in Ws]
+        e1.record()
+        torch.cuda.synchronize()
+        ms += e0.elapsed_time(e1)
+        for W, w in zip(Ws, ws):
+            params += W.numel()
+            stored += w.packed.numel() + w.code8.numel() + 4 * w.c2.numel() + 4 * w.mean.numel()
+        del Ws, ws
+    torch.cuda.empty_cache()
+    nbytes = params * (4 + 0.5 + 1 / 64 + 4 / 16384)
+    return dict(layers=cfg.layers, params=int(params), ms_total=round(ms, 2), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                stored_bytes=int(stored), bits_per_param=round(8.0 * stored / params, 6),
+                note="weights drawn on the device per layer (not timed); includes workspace allocation by the Python binding")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -349,6 +396,13 @@ def main():
         extras["small_m"] = small_m_bench(q, torch, workloads, workloads.CONFIGS[2], dev)
         log("quantize")
         extras["quantize"] = quantize_bench(q, torch, workloads, cfg, dev)
+        log("33B layer")
+        c3 = workloads.CONFIGS[3]
+        extras["llama33b_layer"] = layer_bench(q, torch, workloads, c3, dev, c3.tokens)
+        log("65B: quantize 80 layers, one layer at 16384 tokens")
+        c4 = workloads.CONFIGS[4]
+        extras["llama65b"] = dict(quantize=model_quantize_bench(q, torch, workloads, c4, dev),
+                                  layer=layer_bench(q, torch, workloads, c4, dev, c4.tokens))
 
     cpu = None
     if not args.no_cpu:
