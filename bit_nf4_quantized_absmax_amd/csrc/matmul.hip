@@ -35,7 +35,10 @@
 //    column-wise with ds_read_b64_tr_b16 (within a group of 16 lanes, lane i
 //    gets element i % 4 of the 8-byte reads of lanes i / 4 + 4 e, e = 0..3),
 //    which yields the 8-consecutive-n operands without a transposed store.
-//  * Operands of MFMA sub-step s + 1 are read while sub-step s multiplies.
+//  * Operands of MFMA sub-step s + 1 are read while sub-step s multiplies,
+//    and the last four MFMAs of a step run after its barrier, covering the
+//    first operand reads of the next step.  The left-operand DMA is issued
+//    from inline asm so that the compiler's LDS wait counts stay exact.
 //  * Tiles are mapped so that consecutive tiles (sharing left-operand rows)
 //    run on the same XCD and its L2.
 //  * Epilogue: accumulators -> bf16 (round to nearest even) -> per-wave LDS
@@ -91,6 +94,21 @@ __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+// One 16-byte-per-lane global -> LDS DMA (lane i lands at dst + 16 i).
+// Written as asm rather than the builtin: the compiler counts a builtin LDS
+// DMA as an LDS access of unknown order, which turns every later LDS wait
+// in the step into a full drain (lgkmcnt(0)) and defeats the operand
+// prefetch.  The asm has no register results; the stage it writes is read
+// only after the end-of-step wait (vmcnt) and barrier.
+__device__ __forceinline__ void dma16(const void *src, uint32_t dst) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+}
+
 // Left operand tile: rows m0 .. m0+255 (clamped to rows - 1: never stored)
 // and columns c0 .. c0+63 (16-byte chunks clamped to the row's last chunk,
 // cols % 8 == 0: finite data that meets zero weights in a contraction tail)
@@ -106,9 +124,8 @@ __device__ __forceinline__ void dma_left(uint8_t *stage, const uint16_t *src, in
     const int chunk = (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1));
     const int grow = min(m0 + row, rows - 1);
     const int gcol = min(c0 + chunk * 8, cols - 8);
-    const int off = __builtin_amdgcn_readfirstlane(u * 1024);
-    __builtin_amdgcn_global_load_lds(src + static_cast<int64_t>(grow) * ld + gcol, QLORA_LDS(stage + off), 16, 0,
-                                     0);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage) + u * 1024);
+    dma16(src + static_cast<int64_t>(grow) * ld + gcol, dst);
   }
 }
 
@@ -137,14 +154,28 @@ __device__ __forceinline__ float nf4_level(const float *nf4, uint32_t off4, int 
   return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(nf4) + ((off4 >> (8 * b)) & 0xffu));
 }
 
-// Chunk c (codes 8 c .. 8 c + 7 of the half block) as 8 bf16 = fl32(level * chat).
-__device__ __forceinline__ uint4 expand_chunk(const WBlock &b, int c, float chat, const float *nf4) {
+// Chunk c (codes 8 c .. 8 c + 7 of the half block): the 8 fp32 levels, then
+// 8 bf16 = fl32(level * chat).  Split so that the table reads can be issued a
+// while before their products are needed.
+__device__ __forceinline__ void chunk_levels(float (&lv)[8], const WBlock &b, int c, const float *nf4) {
   const uint32_t words[4] = {b.p.x, b.p.y, b.p.z, b.p.w};
   const uint32_t lo4 = nf4_lo4(words[c]), hi4 = nf4_hi4(words[c]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lv[2 * q] = nf4_level(nf4, lo4, q);
+    lv[2 * q + 1] = nf4_level(nf4, hi4, q);
+  }
+}
+__device__ __forceinline__ uint4 scale_chunk(const float (&lv)[8], float chat) {
   uint32_t o[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(nf4_level(nf4, lo4, q) * chat, nf4_level(nf4, hi4, q) * chat);
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(lv[2 * q] * chat, lv[2 * q + 1] * chat);
   return make_uint4(o[0], o[1], o[2], o[3]);
+}
+__device__ __forceinline__ uint4 expand_chunk(const WBlock &b, int c, float chat, const float *nf4) {
+  float lv[8];
+  chunk_levels(lv, b, c, nf4);
+  return scale_chunk(lv, chat);
 }
 
 __device__ __forceinline__ bf16x4_t ds_tr16(const uint8_t *p) {
@@ -214,12 +245,15 @@ __device__ __forceinline__ void load_frag(Frag &f, const uint8_t *xs, const uint
   ld_a(3);
 }
 
-__device__ __forceinline__ void mfma_frag(const Frag &f, f32x16_t (&acc)[4][2]) {
+// MFMAs of left fragments i0 .. i1 - 1 (all right fragments).
+template <int i0, int i1>
+__device__ __forceinline__ void mfma_rows(const Frag &f, f32x16_t (&acc)[4][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = i0; i < i1; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
+__device__ __forceinline__ void mfma_frag(const Frag &f, f32x16_t (&acc)[4][2]) { mfma_rows<0, 4>(f, acc); }
 
 // A whole 64-wide step without expansion (the LoRA steps).
 template <bool kDx>
@@ -362,34 +396,58 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   }
   raw_barrier<wait_imm(kBlockLoads, 0)>();
 
-  // Step kt: DMA the left tile of kt + 1 into the other stage, then load the
-  // block of kt + 2 into the registers freed by step kt - 1 (these loads are
-  // the newest memory operations: the end-of-step wait lets them fly while
-  // the DMA must land); multiply stage CUR while expanding the block of kt + 1
-  // (loaded a step ago) into the other weight stage, one chunk per MFMA
-  // sub-step; wait for the DMA and the LDS writes; barrier.
+  // Step kt multiplies stage CUR while expanding the block of kt + 1 (loaded a
+  // step ago) into the other weight stage, DMAs the left tile of kt + 1 into
+  // the other left stage and loads the block of kt + 2 into the registers
+  // freed by step kt - 1 (these loads are the newest memory operations: the
+  // end-of-step wait lets them fly while the DMA must land).  Software
+  // pipelined so that every wave always has MFMAs ready to issue:
+  //  * head: operands of sub-step 0, the block's absmax code and the levels
+  //    of chunk 0 are read while the last four MFMAs of the previous step
+  //    (held back from before the barrier, their operands in registers) run;
+  //  * sub-step s: two MFMAs, then the levels of chunk s and the operands of
+  //    sub-step s + 1 are read, two more MFMAs, then chunk s is scaled and
+  //    written while the last four MFMAs run.
+  Frag fa, fb;   // operands of the even / odd sub-steps
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fb.a[i] = bf16x8_t{};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb.b[j] = bf16x8_t{};
   auto step = [&](auto cur_tag, int kt, WBlock &bn, WBlock &bl) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_tag)::value;
     const uint8_t *xs = CUR ? sX1 : sX0;
     const uint8_t *wr = CUR ? sW1 : sW0;
     uint8_t *xn = CUR ? sX0 : sX1;
     uint8_t *wn = CUR ? sW0 : sW1;
-    // First use of the block of kt + 1 before any newer load is issued: the
-    // wait for it then covers only loads issued a step ago.
-    const float chat = block_chat(bn, kt + 1);
-    asm volatile("" ::"v"(bn.p.x), "v"(bn.p.y), "v"(bn.p.z), "v"(bn.p.w), "v"(chat));
+    float lv[8];
+    load_frag<kDx>(fa, xs, wr, ops, 0);
+    const float t8 = sT8[bn.code];
+    chunk_levels(lv, bn, 0, sNf4);
+    // First use of the whole block of kt + 1 before any newer load is issued:
+    // the wait for it then covers only loads issued a step ago.
+    asm volatile("" ::"v"(bn.p.x), "v"(bn.p.y), "v"(bn.p.z), "v"(bn.p.w), "v"(bn.c2));
     __builtin_amdgcn_sched_barrier(0);
+    mfma_rows<2, 3>(fb, acc);
     dma_left(xn, L, Kc, m0, M, min(kt + 1, KT - 1) * kBK, Kc, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
+    mfma_rows<3, 4>(fb, acc);
     block_load(bl, min(kt + 2, KT - 1));
     __builtin_amdgcn_sched_barrier(0);
-    Frag f[2];
-    load_frag<kDx>(f[0], xs, wr, ops, 0);
+    const float c = decode_absmax(t8, bn.c2, mean);
+    const float chat = (kDx && kBK * (kt + 1) + trow >= N) ? 0.f : c;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s < 3) load_frag<kDx>(f[(s + 1) & 1], xs, wr, ops, s + 1);
-      put_chunk(wn, s, expand_chunk(bn, s, chat, sNf4));
-      mfma_frag(f[s & 1], acc);
+      Frag &cur = (s & 1) ? fb : fa;
+      Frag &nxt = (s & 1) ? fa : fb;
+      mfma_rows<0, 1>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s > 0) chunk_levels(lv, bn, s, sNf4);
+      if (s < 3) load_frag<kDx>(nxt, xs, wr, ops, s + 1);
+      mfma_rows<1, 2>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      put_chunk(wn, s, scale_chunk(lv, chat));
+      if (s < 3) mfma_rows<2, 4>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
     raw_barrier<wait_imm(kBlockLoads, 0)>();
   };
@@ -401,6 +459,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
     step(C1(), kt + 1, b0, b1);
   }
   if (kt < KT) step(C0(), kt, b1, b0);
+  mfma_rows<2, 4>(fb, acc);   // held back by the last step
 
   // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A [r, K].
   for (int j0 = 0; j0 < r; j0 += kBK) {
