@@ -53,10 +53,16 @@ int from_hip(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; 
 size_t bf16_bytes(int64_t n) { return round_up(static_cast<size_t>(n) * 2, 256); }
 
 // Workspace of the forward pass.  M <= small_m_max(): the fp32 partials of
-// the down-projection (always needed).  Larger M: T [M, r] when the caller
-// passes no T_out.
-size_t fwd_ws(int64_t M, int64_t K, int32_t r) {
-  if (small_m_ok(M, r)) return small_m_ws_bytes(static_cast<int>(M), static_cast<int>(K), r);
+// the down-projection (always needed), and where the streaming path applies
+// its T copy, split-tile counters and pieces.  Larger M: T [M, r] when the
+// caller passes no T_out.
+size_t fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (small_m_ok(M, r)) {
+    size_t b = small_m_ws_bytes(static_cast<int>(M), static_cast<int>(K), r);
+    if (small_m_stream_ok(M, static_cast<int>(K), r))
+      b = std::max(b, small_m_stream_ws_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), r));
+    return b;
+  }
   return bf16_bytes(M * r);
 }
 
@@ -126,7 +132,7 @@ int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *st
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd) {
   if (M < 0 || N < 1 || K < 64 || K % 64 || N % 8 || r < 1 || r > 128) return 0;
   if (M > 0 && M > kMaxElems / std::max(N, K)) return 0;
-  return is_bwd ? bwd_ws(M, N, K, r).total : fwd_ws(M, K, r);
+  return is_bwd ? bwd_ws(M, N, K, r).total : fwd_ws(M, N, K, r);
 }
 
 int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, int32_t r, float scale,
@@ -217,7 +223,7 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
   if (st) return st;
   if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B) || !bf16_ok(Y) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
   if (small_m_ok(M, r)) {
-    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->cols, r)) return QLORA_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->rows, W->cols, r)) return QLORA_ERR_WORKSPACE;
     SmGroup grp{};
     grp.n = 1;
     grp.M = static_cast<int>(M);
@@ -235,7 +241,7 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
   }
   uint16_t *T = T_out;
   if (!T) {
-    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->cols, r)) return QLORA_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->rows, W->cols, r)) return QLORA_ERR_WORKSPACE;
     T = static_cast<uint16_t *>(ws);
   }
   if (M == 0) return QLORA_OK;
@@ -258,7 +264,7 @@ size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *d,
   size_t total = 0, most = 0;
   for (int i = 0; i < count; ++i) {
     if (!d[i].W || check_linear_shape(M, d[i].W, d[i].r, d[i].scale)) return 0;
-    const size_t b = fwd_ws(M, d[i].W->cols, d[i].r);
+    const size_t b = fwd_ws(M, d[i].W->rows, d[i].W->cols, d[i].r);
     total += b;
     most = std::max(most, b);
   }
@@ -295,7 +301,7 @@ int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, voi
       L.Tout = d[i].T_out;
       L.r = d[i].r;
       L.scale = d[i].scale;
-      p += fwd_ws(M, d[i].W->cols, d[i].r);
+      p += fwd_ws(M, d[i].W->rows, d[i].W->cols, d[i].r);
     }
     return from_hip(launch_small_m(grp, s));
   }

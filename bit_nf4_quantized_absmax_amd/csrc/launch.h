@@ -85,6 +85,13 @@ bool small_m_gemv_xl(const SmGroup &grp);
 int small_m_gemv_slices(int K);
 hipError_t launch_small_m_down_gemv(SmGroup &grp, hipStream_t s);
 hipError_t launch_small_m_gemv(SmGroup &grp, hipStream_t s);
+// Streaming path for 4 < M <= 64, K % 256 == 0 (down-projection, T and the
+// product in three kernels); every linear's P is the start of its workspace
+// region of small_m_stream_ws_bytes.
+bool small_m_stream_ok(int64_t M, int K, int r);
+bool small_m_stream_group_ok(const SmGroup &grp);
+size_t small_m_stream_ws_bytes(int M, int N, int K, int r);
+hipError_t launch_small_m_stream(SmGroup &grp, hipStream_t s);
 // Small-M form of launch_matmul_fwd with T given (requires small_m_ok).
 hipError_t launch_small_m_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T, const uint16_t *B,
                               int r, uint16_t *Y, hipStream_t s);

@@ -47,6 +47,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace qlora {
 
@@ -92,21 +93,6 @@ __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_sched_barrier(0);
-}
-
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
-}
-
-// One 16-byte-per-lane global -> LDS DMA (lane i lands at dst + 16 i).
-// Written as asm rather than the builtin: the compiler counts a builtin LDS
-// DMA as an LDS access of unknown order, which turns every later LDS wait
-// in the step into a full drain (lgkmcnt(0)) and defeats the operand
-// prefetch.  The asm has no register results; the stage it writes is read
-// only after the end-of-step wait (vmcnt) and barrier.
-__device__ __forceinline__ void dma16(const void *src, uint32_t dst) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
 }
 
 // Left operand tile: rows m0 .. m0+255 (clamped to rows - 1: never stored)
