@@ -65,7 +65,6 @@ constexpr int kBN = 256;                  // output columns per tile
 constexpr int kBK = 64;                   // contraction step
 constexpr int kThreadsMM = 512;
 constexpr int kStageBytes = 256 * 64 * 2; // every stage holds 256 x 64 bf16
-constexpr int kBlockLoads = 3;            // VMEM loads per thread for half a weight block
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); vm = 63 / lgkm = 15 do not wait.
@@ -327,16 +326,19 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
 
   // This thread's half block in contraction step kt (half = tid % 2):
   //   forward: row n = c0 + tid / 2 (an output column), k = 64 kt
-  //   dX:      row n = 64 kt + tid / 8 (a contraction index),
-  //            k = c0 + 64 ((tid / 2) % 4)
+  //   dX:      row n = 64 kt + trow (a contraction index), k = c0 + 64 tkb,
+  //            lane bits (half, tkb % 2, row / 4 % 4, row % 4) and wave bits
+  //            (row / 16, tkb / 2): each 16-lane cycle of an expansion write
+  //            covers rows r, r + 4, r + 8, r + 12 and the four (tkb % 2,
+  //            half) pairs, which the [64][256] swizzle maps to 16 distinct
+  //            4-bank groups (no bank conflicts).
   // Neighbouring lanes read neighbouring bytes of a row (the two halves of a
-  // block; in dX the 8 lanes of a row cover its 4 blocks, one 128-byte line),
-  // so a load instruction touches few cache lines.  Rows past N (dX
-  // contraction tail) expand to exact zeros; columns past the matrix are
-  // clamped (never stored).
+  // block, and in dX two neighbouring blocks: 64 contiguous bytes), so a load
+  // instruction touches few cache lines.  Rows past N (dX contraction tail)
+  // expand to exact zeros; columns past the matrix are clamped (never stored).
   const int half = tid & 1;
-  const int trow = kDx ? (tid >> 3) : (tid >> 1);     // row of the tile
-  const int tkb = kDx ? ((tid >> 1) & 3) : 0;         // block within the tile row (dX)
+  const int trow = kDx ? (((lane >> 4) & 3) + 4 * ((lane >> 2) & 3) + 16 * (wave & 3)) : (tid >> 1);
+  const int tkb = kDx ? (((lane >> 1) & 1) + 2 * ((wave >> 2) & 1)) : 0;   // block within the tile row (dX)
   auto block_load = [&](WBlock &b, int kt) __attribute__((always_inline)) {
     if (kDx)
       load_block(b, w, min(kBK * kt + trow, N - 1), min(c0 + 64 * tkb, K - 64), half);
@@ -380,13 +382,16 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
 #pragma unroll
     for (int c = 0; c < 4; ++c) put_chunk(sW0, c, expand_chunk(b0, c, chat, sNf4));
   }
-  raw_barrier<wait_imm(kBlockLoads, 0)>();
+  raw_barrier<wait_imm(0, 0)>();
 
   // Step kt multiplies stage CUR while expanding the block of kt + 1 (loaded a
   // step ago) into the other weight stage, DMAs the left tile of kt + 1 into
   // the other left stage and loads the block of kt + 2 into the registers
-  // freed by step kt - 1 (these loads are the newest memory operations: the
-  // end-of-step wait lets them fly while the DMA must land).  Software
+  // freed by step kt - 1.  The end-of-step barrier waits for all of this
+  // wave's memory operations: the vector-memory counter is only relied on to
+  // retire LDS DMAs in order among themselves, not against the register
+  // loads issued after them (a partial count there let a DMA still be in
+  // flight at the barrier).  Software
   // pipelined so that every wave always has MFMAs ready to issue:
   //  * head: operands of sub-step 0, the block's absmax code and the levels
   //    of chunk 0 are read while the last four MFMAs of the previous step
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
       if (s < 3) mfma_rows<2, 4>(cur, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    raw_barrier<wait_imm(kBlockLoads, 0)>();
+    raw_barrier<wait_imm(0, 0)>();
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;

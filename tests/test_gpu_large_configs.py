@@ -92,3 +92,36 @@ def test_llama65b_quantize_80_layers():
     bits = 8.0 * stored / params
     print("65B: %d params, %d bytes stored, %.6f bits/param" % (params, stored, bits), flush=True)
     assert 4.126953 <= bits <= 4.126954
+
+
+@pytest.mark.parametrize("kernel", ["fwd", "dx"])
+def test_fused_matmul_repeat_bit_identical(kernel):
+    """Sixteen repeated calls of a fused NF4 matmul at the 65B gate_proj shape
+    (M = 16384, N = 22016, K = 8192, r = 64) give bit-identical outputs.  The
+    kernels reuse their LDS stages every step, so an unfinished DMA or
+    expansion write at a step boundary shows up as an occasional tile that
+    differs from one call to the next."""
+    M, N, K, r = 16384, 22016, 8192, 64
+    print("repeat case", kernel, (M, N, K, r), flush=True)
+    w = q.NF4Weight.quantize(workloads.device_normal((N, K), 0.02, 11, DEV))
+    if kernel == "fwd":
+        L = workloads.device_normal((M, K), 1.0, 12, DEV, torch.bfloat16)
+        R = workloads.device_normal((N, r), 0.01, 14, DEV, torch.bfloat16)
+        call = lambda out: q.nf4_matmul_fwd(L, w, Ln, R, out=out)
+    else:
+        L = workloads.device_normal((M, N), 1.0, 12, DEV, torch.bfloat16)
+        R = workloads.device_normal((r, K), 0.01, 14, DEV, torch.bfloat16)
+        call = lambda out: q.nf4_matmul_dx(L, w, Ln, R, out=out)
+    Ln = workloads.device_normal((M, r), 1.0, 13, DEV, torch.bfloat16)
+    ref = call(None)
+    assert not bool(torch.isnan(ref).any())
+    out = torch.empty_like(ref)
+    for i in range(16):
+        out.fill_(float("nan"))
+        call(out)
+        diff = (out != ref).nonzero()
+        if diff.numel():
+            tiles = sorted({(int(a) // 256, int(b) // 256) for a, b in diff[:4096].cpu().numpy()})
+            raise AssertionError("call %d: %d elements differ, tiles %s" % (i + 1, diff.shape[0], tiles[:8]))
+    del w, L, R, Ln, ref, out
+    torch.cuda.empty_cache()
