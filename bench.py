@@ -22,7 +22,7 @@ Also reported on the same JSON line:
   quantize      quantize throughput on the 7 weights (algorithmic GB/s)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
-                       [--copy-probe-mib MiB]
+                       [--copy-probe-mib MiB] [--small-m-only [--small-m-eager]]
 """
 
 import argparse
@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="skip small-M and quantize figures")
+    p.add_argument("--small-m-only", action="store_true",
+                   help="only the small-M (decode) figures, as one JSON line (for profiling that path)")
+    p.add_argument("--small-m-eager", action="store_true",
+                   help="with --small-m-only: eager calls instead of graph replays (counter passes)")
     p.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB first (a reference "
@@ -66,7 +70,8 @@ def small_m_bytes(M, N, K, r):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "matmul_llama7b_m8192_hbm_traffic.md")
-MATMUL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_absmax_amd", "csrc", f) for f in ("matmul.hip", "common.h")]
+MATMUL_SOURCES = [os.path.join(ROOT, "bit_nf4_quantized_absmax_amd", "csrc", f)
+                  for f in ("matmul.hip", "common.h", "lds_dma.h")]
 
 
 def matmul_source_sha256():
@@ -168,14 +173,19 @@ def cpu_baseline(cfg, tokens):
                        "tokens, %.1f s; rate = algorithmic FLOP / time" % (tokens, total_s))
 
 
-def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
+def small_m_bench(q, torch, workloads, cfg, dev, reps=50, graphs=True):
     """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache).
 
     Two launch patterns, each captured once in a HIP graph and replayed (the
     library makes no allocation and no memset inside a call):
-      per_linear  7 linear_fwd calls per layer (2 launches each)
-      grouped     one linear_fwd_group call over the 7 linears (2 launches)
-    GB/s = algorithmic bytes of the 7 linears / time per layer."""
+      per_linear  7 linear_fwd calls per layer
+      grouped     one linear_fwd_group call over the 7 linears
+    A call is 2 launches at M <= 4 (down-projection, dequant-GEMV) and, for
+    4 < M <= 64, 4 (down-projection chunks, T, weight stream, tile epilogue)
+    except single-linear calls at M <= 16, which take the 2-launch path.
+    GB/s = algorithmic bytes of the 7 linears / time per layer.  graphs=False
+    replays the calls eagerly instead (for counter passes, which do not
+    support graph replays)."""
     import ctypes
     from bit_nf4_quantized_absmax_amd._capi import LinearDescStruct
     r = cfg.rank
@@ -223,11 +233,18 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
             for si in range(len(sets)):
                 fn(si)
             torch.cuda.synchronize()
-            stream = torch.cuda.Stream()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                for si in range(len(sets)):
-                    fn(si)
+            if graphs:
+                stream = torch.cuda.Stream()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    for si in range(len(sets)):
+                        fn(si)
+            else:
+                class _Eager:
+                    def replay(self):
+                        for si in range(len(sets)):
+                            fn(si)
+                graph = _Eager()
             for _ in range(3):
                 graph.replay()
             torch.cuda.synchronize()
@@ -241,8 +258,8 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=50):
             gbs = nbytes / (us * 1e-6) / 1e9
             res[name] = dict(us_per_layer=round(us, 2), GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
             del graph
-        res["per_linear"]["launches_per_layer"] = 2 * len(cfg.linears)
-        res["grouped"]["launches_per_layer"] = 2
+        res["per_linear"]["launches_per_layer"] = (2 if M <= 16 else 4) * len(cfg.linears)
+        res["grouped"]["launches_per_layer"] = 2 if M <= 4 else 4
         res["bytes_per_layer"] = int(nbytes)
         out["M%d" % M] = res
     del sets
@@ -343,6 +360,13 @@ def main():
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
+    if args.small_m_only:
+        c2 = workloads.CONFIGS[2]
+        sm = small_m_bench(q, torch, workloads, c2, dev, reps=5 if args.small_m_eager else 50,
+                           graphs=not args.small_m_eager)
+        print(json.dumps(dict(metric="small-M dequant forward GB/s (7B layer, 7 linears, 4 weight sets)",
+                              unit="GB/s", data="synthetic", small_m=sm)), flush=True)
+        return
     cfg = workloads.CONFIGS[1]
     scale = cfg.scale
     log("building inputs for", cfg.name)

@@ -379,7 +379,9 @@ static void sm_launch_main(bool p, int grid, const SmGroup &grp, hipStream_t s) 
 }
 
 hipError_t launch_small_m(SmGroup &grp, hipStream_t s) {
-  if (small_m_stream_group_ok(grp)) return launch_small_m_stream(grp, s);
+  // The streaming path takes four launches; a single linear at M <= 16 is
+  // launch-bound and takes the two-launch path below instead.
+  if (small_m_stream_group_ok(grp) && (grp.n > 1 || grp.M > 16)) return launch_small_m_stream(grp, s);
   if (grp.M <= small_m_gemv_max() && small_m_gemv_xl(grp)) {
     bool any_p = false;
     for (int i = 0; i < grp.n; ++i) {
