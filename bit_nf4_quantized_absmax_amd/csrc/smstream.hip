@@ -4,7 +4,7 @@
 // (automatone.win, "QLoRA paper explained", How it works: the 4-bit weights
 // are dequantized on the fly for the math and never stored in 16-bit.)
 //
-// The work is bound by the packed-weight stream from HBM; three kernels:
+// The work is bound by the packed-weight stream from HBM; four kernels:
 //  * k_ss_down: partial down-projections X[:, c] A[:, c]^T per 256-column
 //    chunk c (fp32), one workgroup per (linear, chunk, 64 adapter rows);
 //  * k_ss_finish: T = bf16(s * sum of the partials in chunk order) (also to
@@ -14,12 +14,10 @@
 //    column and every workgroup takes an equal contiguous range, so each CU
 //    streams the same number of bytes.  A unit's packed bytes (64 rows x 128
 //    bytes: whole cache lines), block codes, group scales and X columns
-//    (16 kMB token rows x 512 bytes) are DMA'd global -> LDS several units
-//    ahead; the weight stream runs one unit further ahead than X (the DMA
-//    completion counter is in order, so the X of the next unit is issued
-//    before the newest weight bytes and the end-of-unit wait leaves those in
-//    flight).  Nothing else in the loop touches global memory, so no wait
-//    ever drains the DMA stream.  Wave (rh, kq) multiplies rows 32 rh .. +31
+//    (16 kMB token rows x 512 bytes) are DMA'd global -> LDS two units ahead
+//    into three-stage rings.  Only LDS DMAs touch global memory in the loop,
+//    so the end-of-unit wait can count them in issue order and leave the
+//    newest unit's DMAs in flight; no wait ever drains the DMA stream.  Wave (rh, kq) multiplies rows 32 rh .. +31
 //    by block kq of the unit: lane (n = l % 16, g = l / 16) takes codes
 //    16 g .. 16 g + 15 of its row's block, expands them through a
 //    byte -> bf16x2 table of the NF4 levels (32 copies, one per lane of a half
@@ -61,13 +59,6 @@ constexpr int kSsLutCopies = 32;
 constexpr int kSsMaxGrid = 256;                   // workgroups of the stream kernel (at most)
 constexpr int kSsDownThreads = 256;
 constexpr int kSsMaxKT = 64;                      // K <= 16384 on this path
-
-// X stages per token-tile count (the weight stream keeps one more); sized to
-// the 160 KB of LDS next to the table and the tile-sum space.
-template <int kMB>
-constexpr int ss_xstages() {
-  return kMB == 1 ? 6 : (kMB == 2 ? 4 : 2);
-}
 
 // s_waitcnt immediate (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int ss_wait(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | 0x70 | ((lgkm & 15) << 8); }
