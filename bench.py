@@ -10,14 +10,16 @@ weights already quantized and every input resident in HBM:
     T = X A^T;  Y = X deq(W)^T + s T B^T;  G = dY B;
     dX = dY deq(W) + s G A;  dA = s G^T X;  dB = s dY^T T.
 Metric: algorithmic TFLOP/s = sum over linears of 4 M N K + 6 M r (N + K)
-per step, divided by the step time.
+per step, divided by the mean step time of the timed steps (HIP events on
+the launch stream; step_ms gives the median and minimum single step).
 
 Also reported on the same JSON line:
   roofline      the dominant kernel (fused dequant matmul), timed with HIP
                 events around each of its launches inside the timed region
   cpu_baseline  the CPU oracle on a bounded token sample of the same step
   small_m       forward-only M = 1 / 16 / 64 over 4 weight sets (> the 256 MB
-                Infinity Cache), replayed from HIP graphs, algorithmic HBM GB/s:
+                Infinity Cache), replayed from HIP graphs (200 replays, mean,
+                median and minimum per layer), algorithmic HBM GB/s:
                 7 single-linear calls per layer and one grouped call
   quantize      quantize throughput on the 7 weights (algorithmic GB/s)
 
@@ -46,7 +48,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-extras", action="store_true", help="skip small-M and quantize figures")
     p.add_argument("--small-m-only", action="store_true",
@@ -173,7 +175,7 @@ def cpu_baseline(cfg, tokens):
                        "tokens, %.1f s; rate = algorithmic FLOP / time" % (tokens, total_s))
 
 
-def small_m_bench(q, torch, workloads, cfg, dev, reps=50, graphs=True):
+def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True):
     """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache).
 
     Two launch patterns, each captured once in a HIP graph and replayed (the
@@ -248,15 +250,17 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=50, graphs=True):
             for _ in range(3):
                 graph.replay()
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            evs[0].record()
+            for i in range(reps):
                 graph.replay()
-            e1.record()
+                evs[i + 1].record()
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+            us = evs[0].elapsed_time(evs[-1]) * 1e3 / (reps * len(sets))
+            per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / len(sets) for i in range(reps))
             gbs = nbytes / (us * 1e-6) / 1e9
-            res[name] = dict(us_per_layer=round(us, 2), GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+            res[name] = dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
+                             reps=reps, GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
             del graph
         res["per_linear"]["launches_per_layer"] = (2 if M <= 16 else 4) * len(cfg.linears)
         res["grouped"]["launches_per_layer"] = 2 if M <= 4 else 4
@@ -362,7 +366,7 @@ def main():
         torch.cuda.empty_cache()
     if args.small_m_only:
         c2 = workloads.CONFIGS[2]
-        sm = small_m_bench(q, torch, workloads, c2, dev, reps=5 if args.small_m_eager else 50,
+        sm = small_m_bench(q, torch, workloads, c2, dev, reps=5 if args.small_m_eager else 200,
                            graphs=not args.small_m_eager)
         print(json.dumps(dict(metric="small-M dequant forward GB/s (7B layer, 7 linears, 4 weight sets)",
                               unit="GB/s", data="synthetic", small_m=sm)), flush=True)
@@ -382,14 +386,15 @@ def main():
 
     events = {"fwd": [], "dx": []}
     t0 = time.perf_counter()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record()
-    for _ in range(args.steps):
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gev[0].record()
+    for i in range(args.steps):
         run_step(q, torch, layers, scale, events)
-    g1.record()
+        gev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = g0.elapsed_time(g1) / args.steps
+    ms_step = gev[0].elapsed_time(gev[-1]) / args.steps
+    step_ms = sorted(gev[i].elapsed_time(gev[i + 1]) for i in range(args.steps))
     tflops = step_flops / (ms_step * 1e-3) / 1e12
     log("step %.3f ms  %.1f TFLOP/s (wall %.3f s)" % (ms_step, tflops, wall))
 
@@ -441,6 +446,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
