@@ -44,6 +44,22 @@ What the pages fix, and the readings taken where they are silent:
 
 * Decode.  c_hat = fl32(fl32(T8[code8] * c2) + mean), two separate fp32
   roundings (no fused multiply-add); w_tilde = bf16_rne(fl32(NF4[q] * c_hat)).
+
+* The other 4-bit data types.  The pages compare NF4 with plain 4-bit
+  integers, whose 16 levels are evenly spaced, and 4-bit floats, whose levels
+  follow the exponent (automatone.win, "QLoRA paper explained", How it works /
+  4-bit NormalFloat; Results table, FP4 vs NF4).  Everything except the level
+  table is shared (blocks, code rule, packing, double quantization, decode).
+  Readings:
+    fp4   the 4-bit float E2M1 (1 sign bit, 2 exponent bits with bias 1,
+          1 mantissa bit, subnormals at exponent 0; magnitudes 0, 0.5, 1, 1.5,
+          2, 3, 4, 6), divided by its largest magnitude 6 in fp32 so that the
+          block's absmax maps to 6.  Ascending table [-v7 .. -v1, 0, 0, v1 ..
+          v7]: the two zeros are codes 7 and 8; code 8 is never produced.
+    int4  symmetric absmax integers: level k = fl32(k / 7) for the 16
+          two's-complement values k = -8 .. 7, so that the absmax maps to 7;
+          code 0 (-8/7) lies outside [-1, 1] and is never produced.
+  A block whose constant is 0 gets the code of the zero level (7, 7, 8).
 """
 
 import math
@@ -56,6 +72,7 @@ from .bf16 import round_fp32_to_bf16_bits
 BLOCK = 64          # elements per first-level absmax block
 GROUP = 256         # first-level constants per second-level group
 ZERO_CODE = 7       # NF4 code of the exact zero level
+QTYPES = ("nf4", "fp4", "int4")   # 4-bit data types; the index is the stored type id
 ZERO_CODE8 = 127    # T8 code of -0 (where exact zero maps, ties to low)
 
 
@@ -111,6 +128,45 @@ def midpoint_thresholds(levels_fp32):
 
 def nf4_thresholds():
     return midpoint_thresholds(nf4_levels())
+
+
+def fp4_magnitudes():
+    """The 8 non-negative E2M1 values by code 2 e + m: exponent field e (bias
+    1, subnormal at e = 0), mantissa bit m."""
+    out = []
+    for e in range(4):
+        for m in range(2):
+            out.append(m / 2.0 if e == 0 else math.ldexp(1.0 + m / 2.0, e - 1))
+    return np.array(out, dtype=np.float64)
+
+
+def fp4_levels():
+    """16 ascending FP4 levels (E2M1 / 6 in fp32); codes 7 and 8 are both zero."""
+    v = fp4_magnitudes().astype(np.float32) / np.float32(6.0)   # IEEE fp32 division
+    pos = v[1:]
+    return np.concatenate([-pos[::-1], np.zeros(2, np.float32), pos]).astype(np.float32)
+
+
+def int4_levels():
+    """16 ascending Int4 levels fl32(k / 7), k = -8 .. 7; code 8 is zero."""
+    k = np.arange(-8, 8).astype(np.float32)
+    return (k / np.float32(7.0)).astype(np.float32)
+
+
+def q4_levels(qtype="nf4"):
+    """Level table of a 4-bit data type ("nf4", "fp4" or "int4")."""
+    if qtype == "nf4":
+        return nf4_levels()
+    if qtype == "fp4":
+        return fp4_levels()
+    if qtype == "int4":
+        return int4_levels()
+    raise ValueError("unknown 4-bit type %r" % (qtype,))
+
+
+def q4_zero_code(qtype="nf4"):
+    """Code written for every element of a block whose constant is 0."""
+    return {"nf4": ZERO_CODE, "fp4": 7, "int4": 8}[qtype]
 
 
 def t8_magnitudes():
@@ -196,8 +252,9 @@ def _block_view(flat, block, fill):
 # Quantize / dequantize
 # --------------------------------------------------------------------------
 
-def quantize(w):
-    """Quantize a fp32 tensor (any shape, flattened row-major) to NF4 + DQ.
+def quantize(w, qtype="nf4"):
+    """Quantize a fp32 tensor (any shape, flattened row-major) to NF4 + DQ
+    (or to the FP4 / Int4 level table, same format otherwise).
 
     Returns a dict with
       packed  uint8[ceil(n/2)]   NF4 codes, two per byte
@@ -208,6 +265,7 @@ def quantize(w):
                                  level; not part of the stored format)
       codes   uint8[n]           unpacked NF4 codes (convenience)
       n       int
+      qtype   str                "nf4", "fp4" or "int4"
     """
     flat = np.ascontiguousarray(np.asarray(w, dtype=np.float32)).reshape(-1)
     n = len(flat)
@@ -222,8 +280,8 @@ def quantize(w):
     absmax = np.max(np.abs(blocks), axis=1).astype(np.float32)
     safe = np.where(absmax > 0, absmax, np.float32(1.0)).astype(np.float32)
     x = (blocks / safe[:, None]).astype(np.float32)          # fp32 IEEE division
-    codes = nearest_code(x, nf4_thresholds())
-    codes[absmax == 0, :] = ZERO_CODE
+    codes = nearest_code(x, midpoint_thresholds(q4_levels(qtype)))
+    codes[absmax == 0, :] = q4_zero_code(qtype)
     codes = codes.reshape(-1)[:n]
     packed = pack_nibbles(codes)
 
@@ -239,7 +297,7 @@ def quantize(w):
     code8 = code8.reshape(-1)[:nb]
 
     return dict(packed=packed, code8=code8, c2=c2, mean=mean, absmax=absmax,
-                codes=codes, n=n)
+                codes=codes, n=n, qtype=qtype)
 
 
 def decode_constants(code8, c2, mean):
@@ -251,22 +309,22 @@ def decode_constants(code8, c2, mean):
     return (prod + np.float32(mean)).astype(np.float32)
 
 
-def dequantize_fp32(packed, code8, c2, mean, n):
+def dequantize_fp32(packed, code8, c2, mean, n, qtype="nf4"):
     """fl32(NF4[q] * c_hat) for every element, before the bf16 rounding."""
     q = unpack_nibbles(packed, n)
     c_hat = decode_constants(code8, c2, mean)
-    lv = nf4_levels()
+    lv = q4_levels(qtype)
     return (lv[q] * c_hat[np.arange(n) // BLOCK]).astype(np.float32)
 
 
-def dequantize(packed, code8, c2, mean, n):
+def dequantize(packed, code8, c2, mean, n, qtype="nf4"):
     """Dequantized weights as uint16 bf16 bit patterns, shape [n]."""
-    return round_fp32_to_bf16_bits(dequantize_fp32(packed, code8, c2, mean, n))
+    return round_fp32_to_bf16_bits(dequantize_fp32(packed, code8, c2, mean, n, qtype))
 
 
 def dequantize_q(qd):
     """dequantize() applied to the dict returned by quantize()."""
-    return dequantize(qd["packed"], qd["code8"], qd["c2"], qd["mean"], qd["n"])
+    return dequantize(qd["packed"], qd["code8"], qd["c2"], qd["mean"], qd["n"], qd.get("qtype", "nf4"))
 
 
 def storage_bits_per_param(n):
