@@ -22,6 +22,10 @@ Also reported on the same JSON line:
                 median and minimum per layer), algorithmic HBM GB/s:
                 7 single-linear calls per layer and one grouped call
   quantize      quantize throughput on the 7 weights (algorithmic GB/s)
+  q4_types      NF4 / FP4 / Int4 level tables on a 4096 x 4096 weight:
+                reconstruction error, quantize from fp32 and bf16, forward
+  shared_input  LoRA products of q / k / v and gate / up (one X): separate
+                launches against one shared-input launch
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
                        [--copy-probe-mib MiB] [--small-m-only [--small-m-eager]]
@@ -293,6 +297,111 @@ def quantize_bench(q, torch, workloads, cfg, dev, reps=5):
                 note="includes workspace allocation by the Python binding")
 
 
+def q4_types_bench(q, torch, workloads, dev, reps=10):
+    """The three 4-bit level tables (NF4, and FP4 / Int4, the types the pages
+    compare it with) on the 7B q_proj shape, 4096 x 4096 weights N(0, 0.02):
+    relative RMS error of the dequantized weight, quantize time from fp32 and
+    from bf16 input (HBM GB/s: input read + codes and constants written), and
+    the fused forward matmul at M = 8192 (same kernel, other table)."""
+    N = K = 4096
+    M, r = 8192, 64
+    W = workloads.device_normal((N, K), workloads.W_STD, 97000, dev)
+    Wb = W.to(torch.bfloat16)
+    X = workloads.device_normal((M, K), 1.0, 97001, dev, torch.bfloat16)
+    T = workloads.device_normal((M, r), 1.0, 97002, dev, torch.bfloat16)
+    B = workloads.device_normal((N, r), workloads.LORA_STD, 97003, dev, torch.bfloat16)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    w64 = W.to(torch.float64)
+    ref_ms = float(torch.mean(w64 * w64))
+    out_bytes = N * K * (0.5 + 1 / 64 + 4 / 16384)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res, ws = {}, {}
+    for qt in q.Q4_TYPES:
+        w = ws[qt] = q.NF4Weight.quantize(W, qt)
+        err = w.dequantize().to(torch.float64) - w64
+        rel = (float(torch.mean(err * err)) / ref_ms) ** 0.5
+        ms32 = timed(lambda: q.NF4Weight.quantize(W, qt))
+        ms16 = timed(lambda: q.NF4Weight.quantize(Wb, qt))
+        res[qt] = dict(rel_rms_error=round(rel, 5),
+                       quantize_fp32_us=round(ms32 * 1e3, 1),
+                       quantize_fp32_GBps=round((4 * N * K + out_bytes) / (ms32 * 1e-3) / 1e9, 1),
+                       quantize_bf16_us=round(ms16 * 1e3, 1),
+                       quantize_bf16_GBps=round((2 * N * K + out_bytes) / (ms16 * 1e-3) / 1e9, 1))
+        del err
+    # the matmuls in interleaved rounds (the last round is reported), so that
+    # clock ramps do not favour one table
+    flops = 2.0 * M * N * K + 2.0 * M * r * N
+    for _ in range(3):
+        for qt in q.Q4_TYPES:
+            ms_mm = timed(lambda: q.nf4_matmul_fwd(X, ws[qt], T, B, out=Y))
+            res[qt].update(fwd_matmul_us=round(ms_mm * 1e3, 1),
+                           fwd_matmul_TFLOPs=round(flops / (ms_mm * 1e-3) / 1e12, 1))
+    del W, Wb, X, T, B, Y, w64, ws
+    torch.cuda.empty_cache()
+    res["note"] = ("4096 x 4096 weight; quantize times include workspace allocation by the Python binding; "
+                   "matmul at M = 8192, r = 64")
+    return res
+
+
+def shared_input_bench(q, torch, workloads, dev, reps=20):
+    """LoRA products of linears that read the same X at the 7B shapes, M =
+    8192, r = 64: q / k / v (K = 4096, three members) and gate / up (K = 4096,
+    two members).  T = s X A_i^T and dA = G_i^T X, per linear (one launch each)
+    against one shared-input launch; HBM GB/s of the shared launch counts X
+    once plus the adapters and outputs."""
+    M, K, r = 8192, 4096, 64
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    X = workloads.device_normal((M, K), 1.0, 98000, dev, torch.bfloat16)
+    dY = torch.zeros(M, 8, dtype=torch.bfloat16, device=dev)
+    for name, n in (("qkv", 3), ("gate_up", 2)):
+        As = [workloads.device_normal((r, K), workloads.LORA_STD, 98100 + i, dev, torch.bfloat16) for i in range(n)]
+        Gs = [workloads.device_normal((M, r), 0.05, 98200 + i, dev, torch.bfloat16) for i in range(n)]
+        Ts = [torch.empty(M, r, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        dAs = [torch.empty(r, K, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        sc = [0.25] * n
+        gws = torch.empty(max(q.lib().qlora_lora_grads_workspace_bytes(M, 8, K, r), 16), dtype=torch.uint8,
+                          device=dev)
+        dws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+        t_sep = timed(lambda: [q.lora_down(X, A, 0.25, out=T) for A, T in zip(As, Ts)])
+        t_sh = timed(lambda: q.lora_down_shared(X, As, sc, outs=Ts))
+        a_sep = timed(lambda: [q.lora_grads(X, dY, G, G, need_dB=False, workspace=gws) for G in Gs])
+        a_sh = timed(lambda: q.lora_dA_shared(X, Gs, outs=dAs, workspace=dws))
+        t_bytes = 2 * M * K + n * (2 * r * K + 2 * M * r)
+        a_bytes = 2 * M * K + n * (2 * M * r + 2 * r * K)
+        out[name] = dict(members=n,
+                         T_separate_us=round(t_sep, 1), T_shared_us=round(t_sh, 1),
+                         T_shared_GBps=round(t_bytes / (t_sh * 1e-6) / 1e9, 1),
+                         dA_separate_us=round(a_sep, 1), dA_shared_us=round(a_sh, 1),
+                         dA_shared_GBps=round(a_bytes / (a_sh * 1e-6) / 1e9, 1))
+        del As, Gs, Ts, dAs, gws, dws
+    del X, dY
+    torch.cuda.empty_cache()
+    return out
+
+
 def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3):
     """fwd + bwd of all linears of one layer of `cfg` at `tokens` tokens."""
     layers = [Layer(q, torch, workloads, lin, tokens, cfg.rank, 1000 * cfg.index + 10 * i, dev)
@@ -425,6 +534,10 @@ def main():
         extras["small_m"] = small_m_bench(q, torch, workloads, workloads.CONFIGS[2], dev)
         log("quantize")
         extras["quantize"] = quantize_bench(q, torch, workloads, cfg, dev)
+        log("4-bit types")
+        extras["q4_types"] = q4_types_bench(q, torch, workloads, dev)
+        log("shared-input LoRA products")
+        extras["shared_input"] = shared_input_bench(q, torch, workloads, dev)
         log("33B layer")
         c3 = workloads.CONFIGS[3]
         extras["llama33b_layer"] = layer_bench(q, torch, workloads, c3, dev, c3.tokens)

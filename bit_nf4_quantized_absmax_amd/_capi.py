@@ -18,12 +18,13 @@ QLORA_ERR_HIP = -4
 
 EXPORTED = (
     "qlora_status_string", "qlora_version", "qlora_nf4_sizes",
-    "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_dequantize_nf4",
+    "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_quantize_nf4_16", "qlora_dequantize_nf4",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
     "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in_workspace_bytes", "qlora_lora_grad_in",
     "qlora_nf4_matmul_dx",
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
     "qlora_linear_group_workspace_bytes", "qlora_linear_fwd_group",
+    "qlora_lora_down_shared", "qlora_lora_dA_shared_workspace_bytes", "qlora_lora_dA_shared",
 )
 
 
@@ -41,6 +42,7 @@ class NF4WeightStruct(ctypes.Structure):
         ("mean", ctypes.c_void_p),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
+        ("qtype", ctypes.c_int32),
     ]
 
 
@@ -68,6 +70,7 @@ _SIGS = {
     "qlora_nf4_sizes": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "qlora_quantize_workspace_bytes": (_sz, [_i64]),
     "qlora_quantize_nf4": (ctypes.c_int, [_vp, _wp, _vp, _sz, _vp]),
+    "qlora_quantize_nf4_16": (ctypes.c_int, [_vp, ctypes.c_int32, _wp, _vp, _sz, _vp]),
     "qlora_dequantize_nf4": (ctypes.c_int, [_wp, _vp, _vp]),
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, ctypes.c_int]),
     "qlora_linear_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
@@ -82,6 +85,11 @@ _SIGS = {
     "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_group_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(LinearDescStruct), _i64]),
     "qlora_linear_fwd_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearDescStruct), _i64, _vp, _sz, _vp]),
+    "qlora_lora_down_shared": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp),
+                                              ctypes.POINTER(_i32), ctypes.POINTER(_f32), ctypes.POINTER(_vp), _vp]),
+    "qlora_lora_dA_shared_workspace_bytes": (_sz, [_i64, _i64, ctypes.c_int, ctypes.POINTER(_i32)]),
+    "qlora_lora_dA_shared": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
+                                            ctypes.POINTER(_vp), _vp, _sz, _vp]),
 }
 
 

@@ -26,6 +26,7 @@ int check_weight(const qlora_nf4_weight *w) {
   if (!w->packed || !w->code8 || !w->c2 || !w->mean) return QLORA_ERR_INVALID_ARG;
   if (!aligned(w->packed, 16) || !aligned(w->code8, 4) || !aligned(w->c2, 4) || !aligned(w->mean, 4))
     return QLORA_ERR_INVALID_ARG;
+  if (w->qtype < QLORA_Q4_NF4 || w->qtype > QLORA_Q4_INT4) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
 }
 
@@ -45,7 +46,8 @@ bool bf16_ok(const void *p) { return p && aligned(p, 16); }
 bool bf16_opt(const void *p) { return !p || aligned(p, 16); }
 
 NF4View view_of(const qlora_nf4_weight *w) {
-  return NF4View{w->packed, w->code8, w->c2, w->mean, static_cast<int>(w->rows), static_cast<int>(w->cols)};
+  return NF4View{w->packed, w->code8, w->c2, w->mean, static_cast<int>(w->rows), static_cast<int>(w->cols),
+                 static_cast<int>(w->qtype)};
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
@@ -117,7 +119,19 @@ int qlora_quantize_nf4(const float *W, const qlora_nf4_weight *out, void *ws, si
   if (!W || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
   const int64_t n = out->rows * out->cols;
   if (!ws || !aligned(ws, 16) || ws_bytes < quantize_ws_bytes(n)) return QLORA_ERR_WORKSPACE;
-  return from_hip(launch_quantize(W, n, out->packed, out->code8, out->c2, out->mean, ws,
+  return from_hip(launch_quantize(W, 0, n, out->qtype, out->packed, out->code8, out->c2, out->mean, ws,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int qlora_quantize_nf4_16(const uint16_t *W, int32_t in_type, const qlora_nf4_weight *out, void *ws,
+                          size_t ws_bytes, void *stream) {
+  int st = check_weight(out);
+  if (st) return st;
+  if (in_type != QLORA_IN_BF16 && in_type != QLORA_IN_FP16) return QLORA_ERR_INVALID_ARG;
+  if (!W || !aligned(W, 16)) return QLORA_ERR_INVALID_ARG;
+  const int64_t n = out->rows * out->cols;
+  if (!ws || !aligned(ws, 16) || ws_bytes < quantize_ws_bytes(n)) return QLORA_ERR_WORKSPACE;
+  return from_hip(launch_quantize(W, in_type, n, out->qtype, out->packed, out->code8, out->c2, out->mean, ws,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -125,7 +139,7 @@ int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *st
   int st = check_weight(w);
   if (st) return st;
   if (!bf16_ok(out_bf16)) return QLORA_ERR_INVALID_ARG;
-  return from_hip(launch_dequantize(w->packed, w->code8, w->c2, w->mean, w->rows * w->cols, out_bf16,
+  return from_hip(launch_dequantize(w->packed, w->code8, w->c2, w->mean, w->rows * w->cols, w->qtype, out_bf16,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -144,6 +158,46 @@ int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, 
   if (M == 0) return QLORA_OK;
   return from_hip(launch_lora_down(X, static_cast<int>(M), static_cast<int>(K), A, r, scale, T,
                                    static_cast<hipStream_t>(stream)));
+}
+
+// Shared-input members: 1..8, r in [1, 128] each, pointer arrays present.
+static int check_shared(int64_t M, int64_t K, int count, const int32_t *r) {
+  if (M < 0 || count < 1 || count > kLoraMaxShared || !r) return QLORA_ERR_INVALID_ARG;
+  if (K < 8 || K % 8 || (M > 0 && M > kMaxElems / K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  for (int i = 0; i < count; ++i)
+    if (r[i] < 1 || r[i] > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  return QLORA_OK;
+}
+
+int qlora_lora_down_shared(const uint16_t *X, int64_t M, int64_t K, int count, const uint16_t *const *A,
+                           const int32_t *r, const float *scale, uint16_t *const *T, void *stream) {
+  int st = check_shared(M, K, count, r);
+  if (st) return st;
+  if (!A || !scale || !T || !bf16_ok(X)) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i)
+    if (!bf16_ok(A[i]) || !bf16_ok(T[i]) || !isfinite(scale[i])) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_lora_down_shared(X, static_cast<int>(M), static_cast<int>(K), count, A, r, scale, T,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_lora_dA_shared_workspace_bytes(int64_t M, int64_t K, int count, const int32_t *r) {
+  if (check_shared(M, K, count, r)) return 0;
+  return lora_dA_shared_ws_bytes(static_cast<int>(M), static_cast<int>(K), count, r);
+}
+
+int qlora_lora_dA_shared(const uint16_t *X, int64_t M, int64_t K, int count, const uint16_t *const *G,
+                         const int32_t *r, uint16_t *const *dA, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_shared(M, K, count, r);
+  if (st) return st;
+  if (!G || !dA || !bf16_ok(X)) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i)
+    if (!bf16_ok(G[i]) || !bf16_ok(dA[i])) return QLORA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_dA_shared_workspace_bytes(M, K, count, r))
+    return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_lora_dA_shared(X, static_cast<int>(M), static_cast<int>(K), count, G, r, dA, ws,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 size_t qlora_lora_grad_in_workspace_bytes(int64_t N, int32_t r) {
@@ -259,6 +313,14 @@ static bool group_small_m(int count, const qlora_linear_desc *d, int64_t M) {
   return true;
 }
 
+// The decode-regime kernels build one level table per launch: a group whose
+// linears mix 4-bit types runs them one call at a time.
+static bool group_one_type(int count, const qlora_linear_desc *d) {
+  for (int i = 1; i < count; ++i)
+    if (d[i].W->qtype != d[0].W->qtype) return false;
+  return true;
+}
+
 size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *d, int64_t M) {
   if (count < 1 || count > kSmMaxGroup || !d) return 0;
   size_t total = 0, most = 0;
@@ -268,7 +330,8 @@ size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *d,
     total += b;
     most = std::max(most, b);
   }
-  return group_small_m(count, d, M) ? total : most;
+  (void)most;
+  return total;   // decode regime: every linear's partials; larger M: every T at once
 }
 
 int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, void *ws, size_t ws_bytes,
@@ -285,6 +348,17 @@ int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, voi
   if (need && (!ws || !aligned(ws, 16) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (group_small_m(count, d, M) && !group_one_type(count, d)) {
+    char *p = static_cast<char *>(ws);
+    for (int i = 0; i < count; ++i) {
+      const size_t b = fwd_ws(M, d[i].W->rows, d[i].W->cols, d[i].r);
+      int st = qlora_linear_fwd(d[i].X, M, d[i].W, d[i].A, d[i].B, d[i].r, d[i].scale, d[i].Y, d[i].T_out, p, b,
+                                stream);
+      if (st) return st;
+      p += b;
+    }
+    return QLORA_OK;
+  }
   if (group_small_m(count, d, M)) {
     SmGroup grp{};
     grp.n = count;
@@ -305,10 +379,41 @@ int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, voi
     }
     return from_hip(launch_small_m(grp, s));
   }
+  // Larger M: every T first (one launch for the linears that read the same
+  // X), then the fused matmuls.  T lives in T_out or in the linear's slice of
+  // the workspace.
+  uint16_t *T[kSmMaxGroup];
+  char *p = static_cast<char *>(ws);
   for (int i = 0; i < count; ++i) {
-    int st = qlora_linear_fwd(d[i].X, M, d[i].W, d[i].A, d[i].B, d[i].r, d[i].scale, d[i].Y, d[i].T_out, ws,
-                              ws_bytes, stream);
-    if (st) return st;
+    T[i] = d[i].T_out ? d[i].T_out : reinterpret_cast<uint16_t *>(p);
+    p += fwd_ws(M, d[i].W->rows, d[i].W->cols, d[i].r);
+  }
+  const int m = static_cast<int>(M);
+  bool done[kSmMaxGroup] = {};
+  for (int i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    const uint16_t *A[kSmMaxGroup];
+    int32_t r[kSmMaxGroup];
+    float sc[kSmMaxGroup];
+    uint16_t *Ts[kSmMaxGroup];
+    int n = 0;
+    for (int j = i; j < count; ++j) {
+      if (done[j] || d[j].X != d[i].X || d[j].W->cols != d[i].W->cols) continue;
+      done[j] = true;
+      A[n] = d[j].A;
+      r[n] = d[j].r;
+      sc[n] = d[j].scale;
+      Ts[n] = T[j];
+      ++n;
+    }
+    const int K = static_cast<int>(d[i].W->cols);
+    hipError_t e = n > 1 ? launch_lora_down_shared(d[i].X, m, K, n, A, r, sc, Ts, s)
+                         : launch_lora_down(d[i].X, m, K, A[0], r[0], sc[0], Ts[0], s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  for (int i = 0; i < count; ++i) {
+    hipError_t e = launch_matmul_fwd(d[i].X, m, view_of(d[i].W), T[i], d[i].B, d[i].r, d[i].Y, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   return QLORA_OK;
 }

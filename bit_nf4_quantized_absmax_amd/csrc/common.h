@@ -37,6 +37,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
 }
 
+// Code of the zero level of each 4-bit table (NF4, FP4, Int4): written for
+// every element of a block whose constant is 0.
+__device__ __forceinline__ int q4_zero_code(int qtype) { return qtype == 2 ? 8 : 7; }
+
 // Block constant decode: c_hat = fl32(fl32(t8 * c2) + mean), two roundings.
 __device__ __forceinline__ float decode_absmax(float t8_level, float c2, float mean) {
   float prod = t8_level * c2;

@@ -12,10 +12,11 @@ namespace qlora {
 // ---- codec ---------------------------------------------------------------
 // Workspace layout for quantize: absmax fp32 [nb] | tree partials fp64.
 size_t quantize_ws_bytes(int64_t n);
-hipError_t launch_quantize(const float *W, int64_t n, uint8_t *packed, uint8_t *code8, float *c2,
-                           float *mean, void *ws, hipStream_t s);
+// W: fp32 (in_type 0), bf16 (1) or fp16 (2) elements.
+hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uint8_t *packed, uint8_t *code8,
+                           float *c2, float *mean, void *ws, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
-                             const float *mean, int64_t n, uint16_t *out, hipStream_t s);
+                             const float *mean, int64_t n, int qtype, uint16_t *out, hipStream_t s);
 
 // ---- NF4 weight view passed to the matmul kernels ---------------------------
 struct NF4View {
@@ -25,12 +26,38 @@ struct NF4View {
   const float *mean;
   int N;  // rows (output features)
   int K;  // columns (input features), multiple of 64
+  int qtype;  // 4-bit level table: 0 NF4, 1 FP4, 2 Int4 (rows of QLORA_Q4_LEVEL_BITS)
 };
 
 // ---- large-M matmuls (T and G already carry the LoRA scale) ---------------------
 // Y [M, N] = X deq(W)^T + T B^T
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s);
+// ---- LoRA products of linears sharing one input X (q/k/v, gate/up) -----------
+// Member i: R[i] (A_i for T, G_i for dA; rcols[i] columns per row), r[i],
+// scale[i], out[i]; part[i] / plane[i]: its fp32 split partials (dA only).
+constexpr int kLoraMaxShared = 8;
+struct LoraShared {
+  const uint16_t *R[kLoraMaxShared];
+  uint16_t *out[kLoraMaxShared];
+  float *part[kLoraMaxShared];
+  int64_t plane[kLoraMaxShared];
+  float scale[kLoraMaxShared];
+  int rcols[kLoraMaxShared];
+  int r[kLoraMaxShared];
+  int y0[kLoraMaxShared + 1];   // first 64-column chunk of each member (prefix sums)
+  int n;
+};
+// T_i = bf16(scale_i X A_i^T) for every member, X read once (bit-identical
+// to launch_lora_down per member).
+hipError_t launch_lora_down_shared(const uint16_t *X, int M, int K, int n, const uint16_t *const *A, const int *r,
+                                   const float *scale, uint16_t *const *T, hipStream_t s);
+// dA_i = G_i^T X for every member (G_i carries the scale), bit-identical to
+// launch_lora_grad_w(X, G_i, ...) per member; workspace lora_dA_shared_ws_bytes.
+size_t lora_dA_shared_ws_bytes(int M, int K, int n, const int *r);
+hipError_t launch_lora_dA_shared(const uint16_t *X, int M, int K, int n, const uint16_t *const *G, const int *r,
+                                 uint16_t *const *dA, void *ws, hipStream_t s);
+
 // ---- small-M forward (M <= small_m_max()) -------------------------------------
 // One linear of a group: Y = X deq(W)^T + T B^T.  T comes from Tin (bf16,
 // already scaled) or, when P is set, is formed as bf16(scale * sum of the

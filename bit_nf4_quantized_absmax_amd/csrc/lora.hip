@@ -198,18 +198,20 @@ __device__ __forceinline__ void nt_read(const uint32_t (&vo)[4], const uint32_t 
   nt_read_tr_half<kOff, 2>(vo, vt, st);
 }
 
+// One workgroup's tile: rows 32 mt .. +31 of L, output columns j0 .. j0 + 63.
+// The walk over the contraction starts at stage mt % (stages), so a tile's
+// summation order depends only on mt.
 template <bool kRT>
-__global__ __launch_bounds__(kLoThreads) void k_lora_nt(const uint16_t *__restrict__ L, int M, int Kc,
-                                                        const uint16_t *__restrict__ R, int rcols, int r,
-                                                        float scale, uint16_t *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kNtSlots][kNtStage];
+__device__ __forceinline__ void lora_nt_tile(uint8_t (&smem)[kLoWaves][kNtSlots][kNtStage],
+                                             const uint16_t *__restrict__ L, int M, int Kc,
+                                             const uint16_t *__restrict__ R, int rcols, int r, float scale,
+                                             uint16_t *__restrict__ out, int mt, int j0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m0 = blockIdx.x * kNtRows;
-  const int j0 = blockIdx.y * 64;
+  const int m0 = mt * kNtRows;
   const int nst = (Kc + 63) / 64;
   const int n_i = nst > wave ? (nst - wave + kLoWaves - 1) / kLoWaves : 0;
-  const int rot = static_cast<int>(blockIdx.x % static_cast<unsigned>(nst));
+  const int rot = static_cast<int>(static_cast<unsigned>(mt) % static_cast<unsigned>(nst));
   // contraction offset of this wave's i-th stage (rotated, always < Kc for i < n_i)
   auto kof = [&](int i) {
     int t = wave + kLoWaves * i + rot;
@@ -326,6 +328,37 @@ __global__ __launch_bounds__(kLoThreads) void k_lora_nt(const uint16_t *__restri
   }
 }
 
+// Grid (row tiles, 64-column chunks of r).
+template <bool kRT>
+__global__ __launch_bounds__(kLoThreads) void k_lora_nt(const uint16_t *__restrict__ L, int M, int Kc,
+                                                        const uint16_t *__restrict__ R, int rcols, int r,
+                                                        float scale, uint16_t *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kNtSlots][kNtStage];
+  lora_nt_tile<kRT>(smem, L, M, Kc, R, rcols, r, scale, out, blockIdx.x, blockIdx.y * 64);
+}
+
+// Members sharing the left operand (e.g. q, k and v, or gate and up, all
+// reading the same X): member i has its own R (A_i [r_i, K]), r_i, scale and
+// output.  1-D grid over (row tile, member chunk), member chunks fastest and
+// mapped so that the chunks of one row tile run back to back on one XCD:
+// the X rows come from HBM once and from that XCD's L2 for the other chunks.
+// Each output tile is computed exactly as by k_lora_nt.
+template <bool kRT>
+__global__ __launch_bounds__(kLoThreads) void k_lora_nt_shared(const uint16_t *__restrict__ L, int M, int Kc,
+                                                               LoraShared sh) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kNtSlots][kNtStage];
+  const unsigned nb = gridDim.x;
+  unsigned lid = blockIdx.x;
+  if ((nb & 7u) == 0) lid = (blockIdx.x & 7u) * (nb >> 3) + (blockIdx.x >> 3);
+  const int Y = sh.y0[sh.n];
+  const int mt = static_cast<int>(lid / static_cast<unsigned>(Y));
+  const int y = static_cast<int>(lid % static_cast<unsigned>(Y));
+  int i = 0;
+  while (i + 1 < sh.n && y >= sh.y0[i + 1]) ++i;
+  lora_nt_tile<kRT>(smem, L, M, Kc, sh.R[i], sh.rcols[i], sh.r[i], sh.scale[i], sh.out[i], mt,
+                    (y - sh.y0[i]) * 64);
+}
+
 // ===========================================================================
 // k_lora_tn: acc[j][d] = sum_m Q[m][j0 + j] P[m][d0 + d] over an M-split,
 // j, d < 64.  Workgroup (d-tile of 64, split): wave w takes the 32-row
@@ -383,23 +416,24 @@ __device__ __forceinline__ void tn_read(const uint32_t (&vt)[2][2], TnStage &st)
     }
 }
 
-__global__ __launch_bounds__(kLoThreads) void k_lora_tn(const uint16_t *__restrict__ P, int M, int D,
-                                                        const uint16_t *__restrict__ Q, int qcols, int r,
-                                                        int stages_per_split, bool out_j_major,
-                                                        uint16_t *__restrict__ out, float *__restrict__ part,
-                                                        int64_t part_plane, int part_pitch) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kTnSlots][kTnStage];
+// One workgroup's tile: d-tile dt (columns 64 dt .. +63 of P), M-split sp,
+// columns j0 .. j0 + 63 of Q.  The walk over the split starts at stage
+// dt % (stages), so a tile's summation order depends only on (dt, sp).
+__device__ __forceinline__ void lora_tn_tile(uint8_t (&smem)[kLoWaves][kTnSlots][kTnStage],
+                                             const uint16_t *__restrict__ P, int M, int D,
+                                             const uint16_t *__restrict__ Q, int qcols, int r,
+                                             int stages_per_split, bool out_j_major, uint16_t *__restrict__ out,
+                                             float *__restrict__ part, int64_t part_plane, int part_pitch, int dt,
+                                             int sp, int j0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int d0 = blockIdx.x * 64;
-  const int sp = blockIdx.y;
-  const int j0 = blockIdx.z * 64;
+  const int d0 = dt * 64;
   const int nms = (M + kTnRows - 1) / kTnRows;
   const int sbeg = sp * stages_per_split;
   const int count = max(0, min(nms, sbeg + stages_per_split) - sbeg);
   const int mend = min(M, (sbeg + count) * kTnRows);
   const int n_i = count > wave ? (count - wave + kLoWaves - 1) / kLoWaves : 0;
-  const int rot = count > 0 ? static_cast<int>(blockIdx.x % static_cast<unsigned>(count)) : 0;
+  const int rot = count > 0 ? static_cast<int>(static_cast<unsigned>(dt) % static_cast<unsigned>(count)) : 0;
   auto mof = [&](int i) {
     int t = wave + kLoWaves * i + rot;
     if (t >= count) t -= count;
@@ -545,6 +579,39 @@ __global__ __launch_bounds__(kLoThreads) void k_lora_tn(const uint16_t *__restri
   }
 }
 
+// Grid (d-tiles, M-splits, 64-column chunks of r).
+__global__ __launch_bounds__(kLoThreads) void k_lora_tn(const uint16_t *__restrict__ P, int M, int D,
+                                                        const uint16_t *__restrict__ Q, int qcols, int r,
+                                                        int stages_per_split, bool out_j_major,
+                                                        uint16_t *__restrict__ out, float *__restrict__ part,
+                                                        int64_t part_plane, int part_pitch) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kTnSlots][kTnStage];
+  lora_tn_tile(smem, P, M, D, Q, qcols, r, stages_per_split, out_j_major, out, part, part_plane, part_pitch,
+               blockIdx.x, blockIdx.y, blockIdx.z * 64);
+}
+
+// dA of members sharing P = X (q, k, v or gate, up): member i has its own
+// Q = G_i, r_i, output and partial planes.  1-D grid over (d-tile, split,
+// member chunk), member chunks fastest and XCD-mapped as in k_lora_nt_shared,
+// so that the tiles reading one block of X run back to back on one XCD.
+// Each tile is computed exactly as by k_lora_tn.
+__global__ __launch_bounds__(kLoThreads) void k_lora_tn_shared(const uint16_t *__restrict__ P, int M, int D,
+                                                               int splits, int stages_per_split, bool out_j_major,
+                                                               int part_pitch, LoraShared sh) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kTnSlots][kTnStage];
+  const unsigned nb = gridDim.x;
+  unsigned lid = blockIdx.x;
+  if ((nb & 7u) == 0) lid = (blockIdx.x & 7u) * (nb >> 3) + (blockIdx.x >> 3);
+  const unsigned Y = static_cast<unsigned>(sh.y0[sh.n]);
+  const int y = static_cast<int>(lid % Y);
+  const int sp = static_cast<int>((lid / Y) % static_cast<unsigned>(splits));
+  const int dt = static_cast<int>(lid / Y / static_cast<unsigned>(splits));
+  int i = 0;
+  while (i + 1 < sh.n && y >= sh.y0[i + 1]) ++i;
+  lora_tn_tile(smem, P, M, D, sh.R[i], sh.rcols[i], sh.r[i], stages_per_split, out_j_major,
+               sh.part[i] ? nullptr : sh.out[i], sh.part[i], sh.plane[i], part_pitch, dt, sp, (y - sh.y0[i]) * 64);
+}
+
 // out[row][col] = bf16(sum_sp part[sp][row][col]) (splits in order).
 __global__ __launch_bounds__(256) void k_sum_partials(const float *__restrict__ part, int splits,
                                                       int64_t plane, int pitch, int nrow, int ncol,
@@ -641,6 +708,69 @@ size_t lora_grad_ws_bytes(int M, int D, int r) {
   const int jc = (r + 63) / 64;
   const size_t part = sp > 1 ? align256(static_cast<size_t>(sp) * (64 * jc) * (((D + 63) / 64) * 64) * 4) : 0;
   return std::max<size_t>(pad + part, 256);
+}
+
+hipError_t launch_lora_down_shared(const uint16_t *X, int M, int K, int n, const uint16_t *const *A, const int *r,
+                                   const float *scale, uint16_t *const *T, hipStream_t s) {
+  LoraShared sh{};
+  sh.n = n;
+  sh.y0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    sh.R[i] = A[i];
+    sh.out[i] = T[i];
+    sh.scale[i] = scale[i];
+    sh.rcols[i] = r[i];
+    sh.r[i] = r[i];
+    sh.y0[i + 1] = sh.y0[i] + (r[i] + 63) / 64;
+  }
+  const unsigned blocks = static_cast<unsigned>((M + kNtRows - 1) / kNtRows) * static_cast<unsigned>(sh.y0[n]);
+  hipLaunchKernelGGL((k_lora_nt_shared<false>), dim3(blocks), dim3(kLoThreads), 0, s, X, M, K, sh);
+  return hipGetLastError();
+}
+
+// Per member: [padded G (r % 8 != 0)] | [fp32 partials (more than one split)],
+// the layout of lora_grad_ws_bytes, one region after the other.
+size_t lora_dA_shared_ws_bytes(int M, int K, int n, const int *r) {
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) total += lora_grad_ws_bytes(M, K, r[i]);
+  return total;
+}
+
+hipError_t launch_lora_dA_shared(const uint16_t *X, int M, int K, int n, const uint16_t *const *G, const int *r,
+                                 uint16_t *const *dA, void *ws, hipStream_t s) {
+  const int sp = tn_splits(M, K);
+  const int dt = (K + 63) / 64;
+  const int nms = (M + kTnRows - 1) / kTnRows;
+  const int per = (nms + sp - 1) / sp;
+  const int pcol = dt * 64;                    // partial planes [64 jc_i, dt * 64], as in launch_lora_grad_w
+  LoraShared sh{};
+  sh.n = n;
+  sh.y0[0] = 0;
+  char *base = static_cast<char *>(ws);
+  for (int i = 0; i < n; ++i) {
+    const size_t pad = (r[i] & 7) ? align256(static_cast<size_t>(M) * round8(r[i]) * 2) : 0;
+    int qcols = 0;
+    sh.R[i] = padded(G[i], M, r[i], base, qcols, s);
+    sh.rcols[i] = qcols;
+    sh.r[i] = r[i];
+    sh.out[i] = dA[i];
+    const int jc = (r[i] + 63) / 64;
+    sh.part[i] = sp > 1 ? reinterpret_cast<float *>(base + pad) : nullptr;
+    sh.plane[i] = static_cast<int64_t>(64 * jc) * pcol;
+    sh.y0[i + 1] = sh.y0[i] + jc;
+    base += lora_grad_ws_bytes(M, K, r[i]);
+  }
+  const unsigned blocks = static_cast<unsigned>(dt) * static_cast<unsigned>(sp) * static_cast<unsigned>(sh.y0[n]);
+  hipLaunchKernelGGL(k_lora_tn_shared, dim3(blocks), dim3(kLoThreads), 0, s, X, M, K, sp, per, true, pcol, sh);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp == 1) return e;
+  for (int i = 0; i < n; ++i) {
+    hipLaunchKernelGGL(k_sum_partials, dim3(grid_for(static_cast<int64_t>(r[i]) * K)), dim3(256), 0, s, sh.part[i],
+                       sp, sh.plane[i], pcol, r[i], K, dA[i]);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,

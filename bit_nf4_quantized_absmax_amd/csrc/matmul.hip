@@ -53,7 +53,7 @@ namespace qlora {
 
 #define QLORA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-__constant__ uint32_t cMMNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
+__constant__ uint32_t cMMQ4Level[3 * 16] = {QLORA_Q4_LEVEL_BITS};
 __constant__ uint32_t cMMT8Level[256] = {QLORA_T8_LEVEL_BITS};
 
 namespace {
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   for (int i = tid; i < 256; i += kThreadsMM) {
-    if (i < 16) sNf4[i] = u2f(cMMNF4Level[i]);
+    if (i < 16) sNf4[i] = u2f(cMMQ4Level[16 * w.qtype + i]);
     sT8[i] = u2f(cMMT8Level[i]);
   }
 

@@ -17,19 +17,21 @@
 
 namespace qlora {
 
-__constant__ uint32_t cNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
-__constant__ uint32_t cNF4Thresh[15] = {QLORA_NF4_THRESH_BITS};
+__constant__ uint32_t cQ4Level[3 * 16] = {QLORA_Q4_LEVEL_BITS};
+__constant__ uint32_t cQ4Thresh[3 * 15] = {QLORA_Q4_THRESH_BITS};
 __constant__ uint32_t cT8Level[256] = {QLORA_T8_LEVEL_BITS};
 __constant__ uint32_t cT8Thresh[255] = {QLORA_T8_THRESH_BITS};
 
 constexpr int kTreeChunk = 2048;   // elements reduced by one workgroup of k_tree_sum
 constexpr int kThreads = 256;
 
-// Nearest NF4 level, ties to the lower code: number of thresholds below x.
-__device__ __forceinline__ uint32_t nf4_code(float x) {
+// Nearest level of the 4-bit table `qtype`, ties to the lower code: number of
+// thresholds below x.
+__device__ __forceinline__ uint32_t q4_code(float x, int qtype) {
+  const uint32_t *th = cQ4Thresh + 15 * qtype;
   uint32_t q = 0;
 #pragma unroll
-  for (int i = 0; i < 15; ++i) q += (x > u2f(cNF4Thresh[i])) ? 1u : 0u;
+  for (int i = 0; i < 15; ++i) q += (x > u2f(th[i])) ? 1u : 0u;
   return q;
 }
 
@@ -38,22 +40,41 @@ __device__ __forceinline__ uint32_t nf4_code(float x) {
 // 64.  The lane group reduces |w| with cross-lane max, every lane divides its
 // elements by the block absmax and codes them, and writes its 2 packed bytes.
 // Elements past n do not exist: they do not enter the max and pack as 0.
+// The input is fp32 (kIn = 0) or 16-bit bit patterns, bf16 (1) or fp16 (2),
+// which widen to fp32 exactly, so every input type codes its fp32 value.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_quant_blocks(const float *__restrict__ W, int64_t n,
-                                                           uint8_t *__restrict__ packed,
+template <int kIn>
+__device__ __forceinline__ float widen(const void *W, int64_t i) {
+  if (kIn == 0) return static_cast<const float *>(W)[i];
+  const uint16_t h = static_cast<const uint16_t *>(W)[i];
+  if (kIn == 1) return u2f(static_cast<uint32_t>(h) << 16);
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+template <int kIn>
+__global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restrict__ W, int64_t n,
+                                                           int qtype, uint8_t *__restrict__ packed,
                                                            float *__restrict__ absmax) {
+  const uint32_t zero = static_cast<uint32_t>(q4_zero_code(qtype));
   const int64_t nchunks = ((n + kBlock - 1) / kBlock) * 16;  // 4-element chunks, whole blocks
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nchunks; c += stride) {
     const int64_t e = c * 4;
     float w[4];
     const bool full = (e + 3 < n);
-    if (full) {
-      const float4 v = *reinterpret_cast<const float4 *>(W + e);
+    if (full && kIn == 0) {
+      const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(W) + e);
       w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if (full) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(W) + e);
+      const uint32_t hs[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = kIn == 1 ? u2f(hs[i] << 16)
+                        : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hs[i])));
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (e + i < n) ? W[e + i] : 0.0f;
+      for (int i = 0; i < 4; ++i) w[i] = (e + i < n) ? widen<kIn>(W, e + i) : 0.0f;
     }
     float a = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
 #pragma unroll
@@ -62,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const float *__restri
     uint32_t q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      q[i] = (a > 0.0f) ? nf4_code(w[i] / a) : 7u;
+      q[i] = (a > 0.0f) ? q4_code(w[i] / a, qtype) : zero;
       if (e + i >= n) q[i] = 0u;
     }
     const uint32_t b0 = q[0] | (q[1] << 4), b1 = q[2] | (q[3] << 4);
@@ -164,11 +185,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict__ packed,
                                                       const uint8_t *__restrict__ code8,
                                                       const float *__restrict__ c2,
-                                                      const float *__restrict__ mean_p, int64_t n,
+                                                      const float *__restrict__ mean_p, int64_t n, int qtype,
                                                       uint16_t *__restrict__ out) {
   __shared__ float lut[16];
   __shared__ float t8[256];
-  if (threadIdx.x < 16) lut[threadIdx.x] = u2f(cNF4Level[threadIdx.x]);
+  if (threadIdx.x < 16) lut[threadIdx.x] = u2f(cQ4Level[16 * qtype + threadIdx.x]);
   for (int i = threadIdx.x; i < 256; i += kThreads) t8[i] = u2f(cT8Level[i]);
   __syncthreads();
   const float mean = mean_p[0];
@@ -224,16 +245,21 @@ size_t quantize_ws_bytes(int64_t n) {
   return a + 2 * static_cast<size_t>(p1) * 8;
 }
 
-hipError_t launch_quantize(const float *W, int64_t n, uint8_t *packed, uint8_t *code8, float *c2,
-                           float *mean, void *ws, hipStream_t s) {
+hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uint8_t *packed, uint8_t *code8,
+                           float *c2, float *mean, void *ws, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
   float *absmax = static_cast<float *>(ws);
   double *buf0 = reinterpret_cast<double *>(static_cast<char *>(ws) + a);
   double *buf1 = buf0 + tree_partials(nb);
 
-  hipLaunchKernelGGL(k_quant_blocks, dim3(grid_for(nb * 16, kThreads, 16384)), dim3(kThreads), 0, s, W,
-                     n, packed, absmax);
+  const dim3 g1(grid_for(nb * 16, kThreads, 16384));
+  if (in_type == 1)
+    hipLaunchKernelGGL(k_quant_blocks<1>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
+  else if (in_type == 2)
+    hipLaunchKernelGGL(k_quant_blocks<2>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
+  else
+    hipLaunchKernelGGL(k_quant_blocks<0>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
   int64_t len = nb;
   hipLaunchKernelGGL(k_tree_sum<float>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads), 0,
                      s, absmax, len, buf0);
@@ -252,9 +278,9 @@ hipError_t launch_quantize(const float *W, int64_t n, uint8_t *packed, uint8_t *
 }
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
-                             const float *mean, int64_t n, uint16_t *out, hipStream_t s) {
+                             const float *mean, int64_t n, int qtype, uint16_t *out, hipStream_t s) {
   hipLaunchKernelGGL(k_dequant, dim3(grid_for((n + 7) / 8, kThreads, 16384)), dim3(kThreads), 0, s, packed,
-                     code8, c2, mean, n, out);
+                     code8, c2, mean, n, qtype, out);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@
 
 namespace qlora {
 
-__constant__ uint32_t cSmNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
+__constant__ uint32_t cSmQ4Level[3 * 16] = {QLORA_Q4_LEVEL_BITS};
 __constant__ uint32_t cSmT8Level[256] = {QLORA_T8_LEVEL_BITS};
 
 constexpr int kSmMaxM = 64;
@@ -276,11 +276,13 @@ __global__ __launch_bounds__(kSmThreads) void k_sm_main(SmGroup grp) {
   load_batch(wave);
 
   // LUT: thread (wave, lane) writes entries byte = wave + 16 j, j = 0 .. 15,
-  // whose low nibble is `wave` and high nibble j (uniform scalar loads).
+  // whose low nibble is `wave` and high nibble j (uniform scalar loads).  The
+  // linears of a group share one 4-bit type.
   {
-    const float lo = u2f(cSmNF4Level[wave]);
+    const uint32_t *lvt = cSmQ4Level + 16 * grp.lin[0].w.qtype;
+    const float lo = u2f(lvt[wave]);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sLut[64 * (wave + 16 * j) + lane] = pack_bf16x2(lo, u2f(cSmNF4Level[j]));
+    for (int j = 0; j < 16; ++j) sLut[64 * (wave + 16 * j) + lane] = pack_bf16x2(lo, u2f(lvt[j]));
   }
   sT8[threadIdx.x & 255] = t8v;                 // four threads write each entry, same value
   sm_barrier_lds_only();

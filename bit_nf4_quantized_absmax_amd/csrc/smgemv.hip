@@ -34,7 +34,7 @@
 
 namespace qlora {
 
-__constant__ uint32_t cGvNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
+__constant__ uint32_t cGvQ4Level[3 * 16] = {QLORA_Q4_LEVEL_BITS};
 
 constexpr int kGvRows = 4;             // rows per item
 constexpr int kGvChunk = 2048;         // columns per chunk: 64 lanes x 32
@@ -203,10 +203,11 @@ __global__ __launch_bounds__(kXL ? 1024 : 512) void k_sm_gemv(SmGroup grp) {
 
   // Tables (and X) into LDS.
   {
+    const uint32_t *lvt = cGvQ4Level + 16 * grp.lin[0].w.qtype;   // one 4-bit type per group
     for (int e = wave; e < 16; e += kWaves) {
-      const float lo = u2f(cGvNF4Level[e]);
+      const float lo = u2f(lvt[e]);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(cGvNF4Level[j]));
+      for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(lvt[j]));
     }
     if (threadIdx.x < 256) sT8[threadIdx.x] = gv_t8_level(threadIdx.x);
     if constexpr (kXL) {
@@ -459,10 +460,11 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
   // Tables, X and T into LDS (all loads first, then the stores: one latency,
   // overlapping the first weight batch).
   {
+    const uint32_t *lvt = cGvQ4Level + 16 * grp.lin[0].w.qtype;   // one 4-bit type per group
     for (int e = wave; e < 16; e += kWaves) {
-      const float lo = u2f(cGvNF4Level[e]);
+      const float lo = u2f(lvt[e]);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(cGvNF4Level[j]));
+      for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(lvt[j]));
     }
     if (threadIdx.x < 256) sT8[threadIdx.x] = gv_t8_level(threadIdx.x);
     uint4 xr[kGvXJ];

@@ -44,7 +44,7 @@
 
 namespace qlora {
 
-__constant__ uint32_t cSsNF4Level[16] = {QLORA_NF4_LEVEL_BITS};
+__constant__ uint32_t cSsQ4Level[3 * 16] = {QLORA_Q4_LEVEL_BITS};
 __constant__ uint32_t cSsT8Level[256] = {QLORA_T8_LEVEL_BITS};
 
 namespace {
@@ -356,9 +356,10 @@ __global__ __launch_bounds__(kSsThreads) void k_ss_stream(SmGroup grp) {
   const bool gather = wave < 2 * kPT;
   if (u0 >= u1) return;                         // (the grid never exceeds the unit count)
 
+  const int qt = grp.lin[0].w.qtype;            // the linears of a group share one 4-bit type
   for (int i = tid; i < 256 * kSsLutCopies; i += kSsThreads) {
     const int byte = i / kSsLutCopies;
-    sLut[i] = pack_bf16x2(u2f(cSsNF4Level[byte & 15]), u2f(cSsNF4Level[byte >> 4]));
+    sLut[i] = pack_bf16x2(u2f(cSsQ4Level[16 * qt + (byte & 15)]), u2f(cSsQ4Level[16 * qt + (byte >> 4)]));
   }
   if (tid < 256) sT8[tid] = u2f(cSsT8Level[tid]);
   if (tid < grp.n) sMean[tid] = grp.lin[tid].w.mean[0];

@@ -46,11 +46,16 @@ def nf4_sizes(n):
     return pb.value, nb.value, nb2.value
 
 
+Q4_TYPES = ("nf4", "fp4", "int4")   # 4-bit level tables; the index is qlora_q4_type
+
+
 @dataclass
 class NF4Weight:
     """A frozen weight [rows, cols] in NF4 with double-quantized constants.
 
     packed uint8 [ceil(n/2)], code8 uint8 [nb], c2 float32 [nb2], mean float32 [1].
+    qtype names the 4-bit level table ("nf4", or "fp4" / "int4" for the
+    comparison types; the rest of the format is the same).
     """
     packed: torch.Tensor
     code8: torch.Tensor
@@ -58,6 +63,7 @@ class NF4Weight:
     mean: torch.Tensor
     rows: int
     cols: int
+    qtype: str = "nf4"
 
     @property
     def shape(self):
@@ -69,29 +75,41 @@ class NF4Weight:
 
     def struct(self):
         return NF4WeightStruct(self.packed.data_ptr(), self.code8.data_ptr(), self.c2.data_ptr(),
-                               self.mean.data_ptr(), self.rows, self.cols)
+                               self.mean.data_ptr(), self.rows, self.cols, Q4_TYPES.index(self.qtype))
 
     @classmethod
-    def empty(cls, rows, cols, device):
+    def empty(cls, rows, cols, device, qtype="nf4"):
+        if qtype not in Q4_TYPES:
+            raise ValueError("qtype must be one of %s" % (Q4_TYPES,))
         pb, nb, nb2 = nf4_sizes(rows * cols)
         return cls(torch.empty(pb, dtype=torch.uint8, device=device),
                    torch.empty(nb, dtype=torch.uint8, device=device),
                    torch.empty(nb2, dtype=torch.float32, device=device),
-                   torch.empty(1, dtype=torch.float32, device=device), rows, cols)
+                   torch.empty(1, dtype=torch.float32, device=device), rows, cols, qtype)
 
     @classmethod
-    def quantize(cls, W):
-        """Quantize a float32 [rows, cols] device tensor (qlora_quantize_nf4)."""
+    def quantize(cls, W, qtype="nf4"):
+        """Quantize a float32, bfloat16 or float16 [rows, cols] device tensor
+        (qlora_quantize_nf4 / qlora_quantize_nf4_16) with the 4-bit level
+        table `qtype` ("nf4", "fp4" or "int4")."""
         if W.dim() != 2:
             raise ValueError("W must be 2-D [out_features, in_features]")
-        _need(W, torch.float32, "W")
+        in16 = {torch.bfloat16: 1, torch.float16: 2}.get(W.dtype)
+        if in16 is None:
+            _need(W, torch.float32, "W")
+        else:
+            _need(W, W.dtype, "W")
         rows, cols = W.shape
-        w = cls.empty(rows, cols, W.device)
+        w = cls.empty(rows, cols, W.device, qtype)
         ws_bytes = lib().qlora_quantize_workspace_bytes(rows * cols)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=W.device)
         st = w.struct()
-        check(lib().qlora_quantize_nf4(_ptr(W), ctypes.byref(st), _ptr(ws), ws_bytes, _stream(W)),
-              "qlora_quantize_nf4")
+        if in16 is None:
+            check(lib().qlora_quantize_nf4(_ptr(W), ctypes.byref(st), _ptr(ws), ws_bytes, _stream(W)),
+                  "qlora_quantize_nf4")
+        else:
+            check(lib().qlora_quantize_nf4_16(_ptr(W), in16, ctypes.byref(st), _ptr(ws), ws_bytes, _stream(W)),
+                  "qlora_quantize_nf4_16")
         return w
 
     def dequantize(self):
@@ -209,6 +227,56 @@ def lora_down(X, A, scale, out=None):
     T = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
     check(lib().qlora_lora_down(_ptr(X), M, K, _ptr(A), r, float(scale), _ptr(T), _stream(X)), "qlora_lora_down")
     return T
+
+
+def _arrays(ptrs, rs, scales=None):
+    n = len(ptrs)
+    return ((ctypes.c_void_p * n)(*ptrs), (ctypes.c_int32 * n)(*rs),
+            None if scales is None else (ctypes.c_float * n)(*[float(s) for s in scales]))
+
+
+def lora_down_shared(X, As, scales, outs=None):
+    """[T_i = scale_i X A_i^T] for linears that share X (qlora_lora_down_shared):
+    one launch, bit-identical to lora_down per linear."""
+    M, K = X.shape
+    _need(X, torch.bfloat16, "X")
+    if not 1 <= len(As) <= 8 or len(scales) != len(As):
+        raise ValueError("1 to 8 members, one scale each")
+    Ts = []
+    for i, A in enumerate(As):
+        _need(A, torch.bfloat16, "A", (A.shape[0], K))
+        T = outs[i] if outs is not None else torch.empty(M, A.shape[0], dtype=torch.bfloat16, device=X.device)
+        _need(T, torch.bfloat16, "T", (M, A.shape[0]))
+        Ts.append(T)
+    pa, ra, sa = _arrays([A.data_ptr() for A in As], [A.shape[0] for A in As], scales)
+    pt, _, _ = _arrays([T.data_ptr() for T in Ts], [1] * len(Ts))
+    check(lib().qlora_lora_down_shared(_ptr(X), M, K, len(As), pa, ra, sa, pt, _stream(X)), "qlora_lora_down_shared")
+    return Ts
+
+
+def lora_dA_shared(X, Gs, outs=None, workspace=None):
+    """[dA_i = G_i^T X] for linears that share X (qlora_lora_dA_shared; G_i
+    carries the scale): one launch (+ the split sums), bit-identical to the dA
+    of lora_grads per linear."""
+    M, K = X.shape
+    _need(X, torch.bfloat16, "X")
+    if not 1 <= len(Gs) <= 8:
+        raise ValueError("1 to 8 members")
+    dAs = []
+    for i, G in enumerate(Gs):
+        _need(G, torch.bfloat16, "G", (M, G.shape[1]))
+        dA = outs[i] if outs is not None else torch.empty(G.shape[1], K, dtype=torch.bfloat16, device=X.device)
+        _need(dA, torch.bfloat16, "dA", (G.shape[1], K))
+        dAs.append(dA)
+    pg, ra, _ = _arrays([G.data_ptr() for G in Gs], [G.shape[1] for G in Gs])
+    pd, _, _ = _arrays([dA.data_ptr() for dA in dAs], [1] * len(dAs))
+    ws_bytes = lib().qlora_lora_dA_shared_workspace_bytes(M, K, len(Gs), ra)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=X.device)
+    if ws.numel() * ws.element_size() < ws_bytes:
+        raise ValueError("workspace smaller than %d bytes" % ws_bytes)
+    check(lib().qlora_lora_dA_shared(_ptr(X), M, K, len(Gs), pg, ra, pd, _ptr(ws), ws_bytes, _stream(X)),
+          "qlora_lora_dA_shared")
+    return dAs
 
 
 def nf4_matmul_fwd(X, w, T, B, out=None):

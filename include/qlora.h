@@ -51,10 +51,22 @@ typedef enum {
   QLORA_ERR_HIP = -4                /* a HIP runtime call or kernel launch failed */
 } qlora_status;
 
+/* 4-bit data types of the first-level codes: the 16-entry level table the
+ * codes index.  Everything else in the format (blocks of 64, nearest level
+ * with ties to the lower code, packing, the double-quantized constants) is
+ * shared.  The pages compare NF4 with evenly spaced 4-bit integers and
+ * exponent-spaced 4-bit floats (automatone.win, "QLoRA paper explained",
+ * 4-bit NormalFloat; Results, FP4 vs NF4).
+ *   NF4   quantiles of N(0, 1) with an exact zero, normalised to [-1, 1]
+ *   FP4   E2M1 floats (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) / 6, ascending,
+ *         codes 7 and 8 both zero (8 is never produced)
+ *   INT4  k / 7 for k = -8 .. 7 (code 0, -8/7, is never produced) */
+typedef enum { QLORA_Q4_NF4 = 0, QLORA_Q4_FP4 = 1, QLORA_Q4_INT4 = 2 } qlora_q4_type;
+
 /* One quantized weight W [rows = N, cols = K], n = rows * cols elements,
  * flattened row-major.  Block b covers elements [64 b, 64 b + 64); group g
  * covers blocks [256 g, 256 g + 256); the last block and group may be partial.
- *   packed  [ceil(n/2)]   NF4 codes: byte j holds element 2j in its low
+ *   packed  [ceil(n/2)]   4-bit codes: byte j holds element 2j in its low
  *                         nibble and element 2j+1 in its high nibble; for odd
  *                         n the last high nibble is 0.
  *   code8   [nb]          8-bit code of block b's absmax, an index into the
@@ -70,6 +82,10 @@ typedef struct {
   float *mean;
   int64_t rows;
   int64_t cols;
+  int32_t qtype;   /* qlora_q4_type; 0 (NF4) for a zero-initialised struct.
+                      Set before qlora_quantize_nf4, which codes with this
+                      type's table; every other call decodes with it.  A
+                      value outside the enum is QLORA_ERR_INVALID_ARG. */
 } qlora_nf4_weight;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -97,6 +113,19 @@ size_t qlora_quantize_workspace_bytes(int64_t n);
 int qlora_quantize_nf4(const float *W, const qlora_nf4_weight *out, void *ws,
                        size_t ws_bytes, void *stream);
 
+/* Element types of a 16-bit weight for qlora_quantize_nf4_16. */
+typedef enum { QLORA_IN_BF16 = 1, QLORA_IN_FP16 = 2 } qlora_in_type;
+
+/* Quantize a 16-bit W [out->rows, out->cols] (bf16 or fp16 bit patterns,
+ * in_type) into *out.  Both types widen to fp32 exactly, so the result is
+ * bit-identical to qlora_quantize_nf4 on the widened fp32 values, without an
+ * fp32 copy of a 16-bit checkpoint.  (The pages load a pretrained model
+ * straight into 4 bits with bf16 compute: creativeworksofknowledge.com,
+ * "QLoRA: Fine-Tune 70B on One GPU", Code.)  Same rules and workspace as
+ * qlora_quantize_nf4; an in_type outside the enum is QLORA_ERR_INVALID_ARG. */
+int qlora_quantize_nf4_16(const uint16_t *W, int32_t in_type, const qlora_nf4_weight *out, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* Dequantize *w to bf16 out [rows, cols]:
  *   c_hat = fl32(fl32(T8[code8] * c2) + mean)      (no fused multiply-add)
  *   out   = bf16_rne(fl32(NF4[q] * c_hat))
@@ -108,7 +137,7 @@ int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *st
  * (is_bwd = 1) at these sizes.  0 if the shape is unsupported, and 0 for a
  * forward pass at M = 0.  A forward pass at 1 <= M <= 64 with r % 8 == 0
  * (the decode regime) always needs its workspace: it holds fp32 partial sums
- * of X A^T, at most 4 x M x r floats. */
+ * of X A^T and, on the streaming route, the weight stream's tile sums and T. */
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd);
 
 /* Forward: Y [M, N] = X [M, K] deq(W)^T + scale (X A^T) B^T.
@@ -118,12 +147,15 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
  *   reuse in the backward pass; when NULL, T lives in the workspace.
  *   ws: device memory of qlora_linear_workspace_bytes(M, N, K, r, 0) bytes,
  *   16-byte aligned; it may be NULL only when that size is 0.
- *   At 1 <= M <= 64 with r % 8 == 0 the pass takes a decode-regime route: two
- *   launches, the second streaming the packed weight once with all of its
- *   loads in flight (bandwidth-bound), which applies each block constant to
- *   the bf16 level product in fp32 (bf16(NF4[q]) * c_hat) instead of rounding
- *   NF4[q] * c_hat to bf16 (within the same tolerance); otherwise two MFMA tile
- *   kernels that dequantize exactly as qlora_dequantize_nf4 does.
+ *   At 1 <= M <= 64 with r % 8 == 0 the pass takes a decode-regime route that
+ *   streams the packed weight once (bandwidth-bound): two launches at M <= 4
+ *   (down-projection, dequant-GEMV) and for a single linear at M <= 16, four
+ *   at 4 < M <= 64 when K % 256 == 0 and K <= 16384 (down-projection chunks,
+ *   T, persistent weight stream, tile epilogue).  These routes apply each
+ *   block constant to the bf16 level product in fp32 (bf16(NF4[q]) * c_hat)
+ *   instead of rounding NF4[q] * c_hat to bf16 (within the same tolerance).
+ *   Otherwise two MFMA tile kernels that dequantize exactly as
+ *   qlora_dequantize_nf4 does.
  * Requires K % 64 == 0 (blocks never straddle rows), 1 <= r <= 128, M >= 0
  * (M = 0 launches nothing), N >= 1.  Pages: automatone.win, "QLoRA paper
  * explained", How it works; creativeworksofknowledge.com, "QLoRA: Fine-Tune
@@ -145,17 +177,43 @@ typedef struct {
   uint16_t *T_out;              /* [M, r], nullable */
 } qlora_linear_desc;
 
+/* Shared-input LoRA products.  In a decoder layer q, k and v read the same
+ * input X, and so do gate and up; the LoRA branch reads X once per linear for
+ * T = s X A^T and once more for dA = G^T X.  These calls take up to 8 linears
+ * ("members") that share X [M, K] and make one launch each, placed so that
+ * every block of X is read from HBM once and served from L2 to the other
+ * members.  Results are bit-identical to qlora_lora_down / the dA of
+ * qlora_lora_grads per member.  Member arrays (A, G, r, scale, T, dA) are
+ * host arrays of `count` entries; the tensors they point to are device
+ * memory with the layouts of the single calls.  Rules: 1 <= count <= 8,
+ * K % 8 == 0, 1 <= r[i] <= 128, finite scales (else INVALID_ARG /
+ * UNSUPPORTED_SHAPE, nothing launched).  Page: automatone.win, "QLoRA paper
+ * explained", How it works (adapters on every linear); creativeworksof
+ * knowledge.com, "QLoRA: Fine-Tune 70B on One GPU", Code (all-linear targets).
+ *   T[i] [M, r[i]] = bf16(scale[i] * X A[i]^T),  A[i] [r[i], K] */
+int qlora_lora_down_shared(const uint16_t *X, int64_t M, int64_t K, int count, const uint16_t *const *A,
+                           const int32_t *r, const float *scale, uint16_t *const *T, void *stream);
+/* dA[i] [r[i], K] = bf16(G[i]^T X),  G[i] [M, r[i]] (already carries the scale);
+ * ws of qlora_lora_dA_shared_workspace_bytes(M, K, count, r) bytes. */
+size_t qlora_lora_dA_shared_workspace_bytes(int64_t M, int64_t K, int count, const int32_t *r);
+int qlora_lora_dA_shared(const uint16_t *X, int64_t M, int64_t K, int count, const uint16_t *const *G,
+                         const int32_t *r, uint16_t *const *dA, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes for qlora_linear_fwd_group (0 if any shape is unsupported,
- * count < 1 or count > 8). */
+ * count < 1 or count > 8): the sum of the linears' forward workspaces. */
 size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *descs, int64_t M);
 
-/* Forward of up to 8 independent linears that share the token count M, each
- * exactly as qlora_linear_fwd computes it (same results, bit for bit).  In
- * the decode regime (1 <= M <= 64, every r % 8 == 0) the whole group takes
- * two launches: one for all the down-projection partials, one streaming all
- * the packed weights, so that launch latency is paid once per group (for
- * example the q, k, v projections of a layer, which share their input).
- * Outside that regime the linears run one after another.  ws: device memory
+/* Forward of up to 8 linears that share the token count M, each as
+ * qlora_linear_fwd computes it.  In the decode regime (1 <= M <= 64, every
+ * r % 8 == 0, one 4-bit type) the whole group takes the launches of one
+ * call, so that launch latency is paid once per group (for example the seven
+ * projections of a layer); on the streaming route (4 < M <= 64) the fp32
+ * summation order depends on the whole group, so results agree with single
+ * calls within the tolerance, elsewhere bit for bit.  A decode-regime group
+ * that mixes 4-bit types runs its linears one call at a time.  At larger M,
+ * linears whose descriptors carry the same X pointer and K (q, k, v; gate,
+ * up) get their T from one qlora_lora_down_shared launch, then every linear
+ * runs its fused matmul; results are bit-identical to single calls.  ws: device memory
  * of qlora_linear_group_workspace_bytes bytes, 16-byte aligned.  Validation of
  * every descriptor happens before any launch.  Pages: automatone.win,
  * "QLoRA paper explained", How it works; creativeworksofknowledge.com,

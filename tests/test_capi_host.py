@@ -20,7 +20,7 @@ OK, INVALID, SHAPE, WS = 0, -1, -2, -3
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qlora_[A-Za-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -123,6 +123,37 @@ def test_validation_rejects_before_launch():
     nulx = (D * 1)(D(0, ctypes.pointer(w), 0x20000, 0x20000, 8, 1.0, 0x20000, 0))
     assert L.qlora_linear_fwd_group(1, nulx, 8, P, 1 << 20, None) == INVALID
     assert L.qlora_linear_fwd_group(1, arr, 0, None, 0, None) == OK
+    # shared-input LoRA products: member count, r range, K % 8, null arrays, workspace, M = 0
+    PA = (ctypes.c_void_p * 3)(0x20000, 0x30000, 0x40000)
+    R3 = (ctypes.c_int32 * 3)(64, 64, 64)
+    S3 = (ctypes.c_float * 3)(0.25, 0.25, 0.25)
+    assert L.qlora_lora_down_shared(P, 8, 64, 0, PA, R3, S3, PA, None) == INVALID
+    assert L.qlora_lora_down_shared(P, 8, 64, 9, PA, R3, S3, PA, None) == INVALID
+    assert L.qlora_lora_down_shared(P, 8, 60, 3, PA, R3, S3, PA, None) == SHAPE
+    assert L.qlora_lora_down_shared(P, 8, 64, 3, PA, (ctypes.c_int32 * 3)(64, 129, 8), S3, PA, None) == SHAPE
+    assert L.qlora_lora_down_shared(P, 8, 64, 3, None, R3, S3, PA, None) == INVALID
+    assert L.qlora_lora_down_shared(P, 8, 64, 3, PA, R3, (ctypes.c_float * 3)(1, float("nan"), 1), PA, None) == INVALID
+    assert L.qlora_lora_down_shared(P, 0, 64, 3, PA, R3, S3, PA, None) == OK
+    assert L.qlora_lora_dA_shared_workspace_bytes(8192, 4096, 3, R3) >= 256
+    assert L.qlora_lora_dA_shared_workspace_bytes(8192, 4096, 9, R3) == 0
+    assert L.qlora_lora_dA_shared(P, 8, 64, 3, PA, R3, PA, None, 0, None) == WS
+    assert L.qlora_lora_dA_shared(P, 8, 64, 3, PA, R3, None, P, 1 << 20, None) == INVALID
+    assert L.qlora_lora_dA_shared(P, 0, 64, 3, PA, R3, PA, P, 1 << 20, None) == OK
+    # 16-bit input quantize: input type outside the enum, null or misaligned input, workspace
+    assert L.qlora_quantize_nf4_16(P, 0, ctypes.byref(w), P, 1 << 20, None) == INVALID
+    assert L.qlora_quantize_nf4_16(P, 3, ctypes.byref(w), P, 1 << 20, None) == INVALID
+    assert L.qlora_quantize_nf4_16(None, 1, ctypes.byref(w), P, 1 << 20, None) == INVALID
+    assert L.qlora_quantize_nf4_16(ctypes.c_void_p(0x20002), 2, ctypes.byref(w), P, 1 << 20, None) == INVALID
+    assert L.qlora_quantize_nf4_16(P, 1, ctypes.byref(w), None, 0, None) == WS
+    # 4-bit type outside the enum (NF4 0, FP4 1, Int4 2)
+    for bad_t in (-1, 3):
+        wt = _capi.NF4WeightStruct(0x10000, 0x11000, 0x12000, 0x13000, 64, 64, bad_t)
+        assert L.qlora_quantize_nf4(P, ctypes.byref(wt), P, 1 << 20, None) == INVALID
+        assert L.qlora_dequantize_nf4(ctypes.byref(wt), P, None) == INVALID
+        assert L.qlora_linear_fwd(P, 8, ctypes.byref(wt), P, P, 8, 1.0, P, P, P, 1 << 20, None) == INVALID
+    for good_t in (1, 2):
+        wt = _capi.NF4WeightStruct(0x10000, 0x11000, 0x12000, 0x13000, 64, 64, good_t)
+        assert L.qlora_linear_fwd(P, 0, ctypes.byref(wt), P, P, 8, 1.0, P, P, None, 0, None) == OK
     # misaligned weight buffers
     mis = _capi.NF4WeightStruct(0x10008, 0x11000, 0x12000, 0x13000, 64, 64)
     assert L.qlora_dequantize_nf4(ctypes.byref(mis), P, None) == INVALID
