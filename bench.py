@@ -26,6 +26,8 @@ Also reported on the same JSON line:
                 reconstruction error, quantize from fp32 and bf16, forward
   shared_input  LoRA products of q / k / v and gate / up (one X): separate
                 launches against one shared-input launch
+  dropout       the 7B step with LoRA dropout p = 0.05 against without, and
+                the keep-mask kernel
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
                        [--copy-probe-mib MiB] [--small-m-only [--small-m-eager]]
@@ -402,6 +404,59 @@ def shared_input_bench(q, torch, workloads, dev, reps=20):
     return out
 
 
+def dropout_bench(q, torch, workloads, cfg, dev, p=0.05, steps=5):
+    """LoRA dropout (p = 0.05, the pages' adapter setting) on the 7B layer at
+    8192 tokens: fwd + bwd of the 7 linears through the composite calls with
+    and without dropout (same algorithmic FLOP), and the keep-mask kernel on
+    X [8192, 4096] (HBM GB/s: X read, X_d written, mask bits written)."""
+    M, r = cfg.tokens, cfg.rank
+    lins = []
+    for i, lin in enumerate(cfg.linears):
+        N, K = lin.out_features, lin.in_features
+        W = workloads.device_normal((N, K), workloads.W_STD, 99000 + i, dev)
+        lins.append(dict(w=q.NF4Weight.quantize(W), N=N, K=K,
+                         X=workloads.device_normal((M, K), 1.0, 99100 + i, dev, torch.bfloat16),
+                         A=workloads.device_normal((r, K), workloads.LORA_STD, 99200 + i, dev, torch.bfloat16),
+                         B=workloads.device_normal((N, r), workloads.LORA_STD, 99300 + i, dev, torch.bfloat16),
+                         dY=workloads.device_normal((M, N), 1.0, 99400 + i, dev, torch.bfloat16)))
+        del W
+    flops = sum(4.0 * M * L["N"] * L["K"] + 6.0 * M * r * (L["N"] + L["K"]) for L in lins)
+
+    def plain():
+        for L in lins:
+            Y, T = q.linear_fwd(L["X"], L["w"], L["A"], L["B"], cfg.scale)
+            q.linear_bwd(L["dY"], L["X"], T, L["w"], L["A"], L["B"], cfg.scale)
+
+    def dropped():
+        for i, L in enumerate(lins):
+            Y, T, keep = q.linear_fwd_dropout(L["X"], L["w"], L["A"], L["B"], cfg.scale, p, 7 + i)
+            q.linear_bwd_dropout(L["dY"], L["X"], T, L["w"], L["A"], L["B"], cfg.scale, p, keep)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_plain = timed(plain, steps)
+    ms_drop = timed(dropped, steps)
+    X = lins[0]["X"]
+    mask_us = timed(lambda: q.dropout_mask(X, p, 1), 20) * 1e3
+    nbytes = X.numel() * 2 * 2 + X.numel() / 8
+    del lins, X
+    torch.cuda.empty_cache()
+    return dict(p=p, plain_ms_per_step=round(ms_plain, 3), dropout_ms_per_step=round(ms_drop, 3),
+                plain_TFLOPs=round(flops / (ms_plain * 1e-3) / 1e12, 1),
+                dropout_TFLOPs=round(flops / (ms_drop * 1e-3) / 1e12, 1),
+                mask_us_8192x4096=round(mask_us, 1), mask_GBps=round(nbytes / (mask_us * 1e-6) / 1e9, 1),
+                note="composite calls (workspaces allocated by the Python binding each call)")
+
+
 def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3):
     """fwd + bwd of all linears of one layer of `cfg` at `tokens` tokens."""
     layers = [Layer(q, torch, workloads, lin, tokens, cfg.rank, 1000 * cfg.index + 10 * i, dev)
@@ -538,6 +593,8 @@ def main():
         extras["q4_types"] = q4_types_bench(q, torch, workloads, dev)
         log("shared-input LoRA products")
         extras["shared_input"] = shared_input_bench(q, torch, workloads, dev)
+        log("LoRA dropout")
+        extras["dropout"] = dropout_bench(q, torch, workloads, cfg, dev)
         log("33B layer")
         c3 = workloads.CONFIGS[3]
         extras["llama33b_layer"] = layer_bench(q, torch, workloads, c3, dev, c3.tokens)

@@ -9,11 +9,13 @@ package only marshals torch tensors to it.
 from ._capi import EXPORTED, LIB_PATH, QLoRAError, lib, status_string  # noqa: F401
 from .ops import (Q4_TYPES, NF4Weight, QLoRALinear, QLoRALinearFn, linear_bwd, linear_fwd,  # noqa: F401
                   linear_fwd_group, lora_dA_shared, lora_down, lora_down_shared, lora_grad_in, lora_grads,
-                  nf4_matmul_dx, nf4_matmul_fwd, nf4_sizes)
+                  nf4_matmul_dx, nf4_matmul_fwd, nf4_sizes, dropout_mask, dropout_apply, nf4_matmul_dx_dropout,
+                  dropout_scale, linear_fwd_dropout, linear_bwd_dropout)
 
 __all__ = [
     "Q4_TYPES", "NF4Weight", "QLoRALinear", "QLoRALinearFn", "linear_fwd", "linear_fwd_group", "linear_bwd", "lora_down",
     "nf4_matmul_fwd", "lora_grad_in", "nf4_matmul_dx", "lora_grads", "nf4_sizes", "lib",
-    "lora_down_shared", "lora_dA_shared",
+    "lora_down_shared", "lora_dA_shared", "dropout_mask", "dropout_apply", "nf4_matmul_dx_dropout",
+    "dropout_scale", "linear_fwd_dropout", "linear_bwd_dropout",
     "QLoRAError", "status_string",
 ]

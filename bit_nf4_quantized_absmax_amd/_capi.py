@@ -25,6 +25,8 @@ EXPORTED = (
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
     "qlora_linear_group_workspace_bytes", "qlora_linear_fwd_group",
     "qlora_lora_down_shared", "qlora_lora_dA_shared_workspace_bytes", "qlora_lora_dA_shared",
+    "qlora_dropout_mask", "qlora_dropout_apply", "qlora_nf4_matmul_dx_dropout",
+    "qlora_linear_dropout_workspace_bytes", "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
 )
 
 
@@ -90,6 +92,14 @@ _SIGS = {
     "qlora_lora_dA_shared_workspace_bytes": (_sz, [_i64, _i64, ctypes.c_int, ctypes.POINTER(_i32)]),
     "qlora_lora_dA_shared": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp), ctypes.POINTER(_i32),
                                             ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "qlora_dropout_mask": (ctypes.c_int, [_vp, _i64, _i64, _f32, ctypes.c_uint64, _vp, _vp, _vp]),
+    "qlora_dropout_apply": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "qlora_nf4_matmul_dx_dropout": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "qlora_linear_dropout_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, ctypes.c_int]),
+    "qlora_linear_fwd_dropout": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _f32, ctypes.c_uint64, _vp,
+                                                _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_bwd_dropout": (ctypes.c_int, [_vp, _vp, _vp, _i64, _wp, _vp, _vp, _i32, _f32, _f32, _vp, _vp,
+                                                _vp, _vp, _vp, _sz, _vp]),
 }
 
 

@@ -463,4 +463,112 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
   return QLORA_OK;
 }
 
+// ---- LoRA dropout -------------------------------------------------------------
+
+static bool drop_p_ok(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
+static uint32_t drop_thresh(float p) { return static_cast<uint32_t>(floor(static_cast<double>(p) * 4294967296.0)); }
+static float drop_scale(float scale, float p) {
+  return static_cast<float>(static_cast<double>(scale) / (1.0 - static_cast<double>(p)));
+}
+
+int qlora_dropout_mask(const uint16_t *X, int64_t M, int64_t K, float p, uint64_t seed, uint16_t *X_drop,
+                       uint32_t *keep, void *stream) {
+  if (M < 0 || !drop_p_ok(p)) return QLORA_ERR_INVALID_ARG;
+  if (K < 32 || K % 32 || (M > 0 && M > kMaxElems / K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!bf16_ok(X) || !bf16_ok(X_drop) || !keep || !aligned(keep, 16)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_dropout_mask(X, M * K, seed, drop_thresh(p), X_drop, keep, static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dropout_apply(const uint16_t *X, int64_t M, int64_t K, const uint32_t *keep, uint16_t *X_drop,
+                        void *stream) {
+  if (M < 0) return QLORA_ERR_INVALID_ARG;
+  if (K < 32 || K % 32 || (M > 0 && M > kMaxElems / K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (!bf16_ok(X) || !bf16_ok(X_drop) || !keep || !aligned(keep, 16)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_dropout_apply(X, M * K, keep, X_drop, static_cast<hipStream_t>(stream)));
+}
+
+int qlora_nf4_matmul_dx_dropout(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W, const uint16_t *G,
+                                const uint16_t *A, int32_t r, const uint32_t *keep, uint16_t *dX, void *stream) {
+  int st = check_linear_shape(M, W, r, 1.0f);
+  if (st) return st;
+  if (!bf16_ok(dY) || !bf16_ok(G) || !bf16_ok(A) || !bf16_ok(dX) || !keep || !aligned(keep, 16))
+    return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  return from_hip(launch_matmul_dx_drop(dY, static_cast<int>(M), view_of(W), G, A, r, keep, dX,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_linear_dropout_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd) {
+  if (M < 0 || N < 1 || K < 64 || K % 64 || N % 8 || r < 1 || r > 128) return 0;
+  if (M > 0 && M > kMaxElems / std::max(N, K)) return 0;
+  const size_t xd = bf16_bytes(M * K);
+  return xd + (is_bwd ? bwd_ws(M, N, K, r).total : bf16_bytes(M * r));
+}
+
+int qlora_linear_fwd_dropout(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *A,
+                             const uint16_t *B, int32_t r, float scale, float p, uint64_t seed, uint16_t *Y,
+                             uint16_t *T_out, uint32_t *keep_out, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!drop_p_ok(p)) return QLORA_ERR_INVALID_ARG;
+  if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B) || !bf16_ok(Y) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
+  if (!keep_out || !aligned(keep_out, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 16) || ws_bytes < qlora_linear_dropout_workspace_bytes(M, W->rows, W->cols, r, 0))
+    return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const NF4View v = view_of(W);
+  const int m = static_cast<int>(M);
+  uint16_t *Xd = static_cast<uint16_t *>(ws);
+  uint16_t *T = T_out ? T_out : reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + bf16_bytes(M * v.K));
+  hipError_t e = launch_dropout_mask(X, M * v.K, seed, drop_thresh(p), Xd, keep_out, s);
+  if (e == hipSuccess) e = launch_lora_down(Xd, m, v.K, A, r, drop_scale(scale, p), T, s);
+  if (e == hipSuccess) e = launch_matmul_fwd(X, m, v, T, B, r, Y, s);
+  return from_hip(e);
+}
+
+int qlora_linear_bwd_dropout(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,
+                             const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
+                             float p, const uint32_t *keep, uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws,
+                             size_t ws_bytes, void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!drop_p_ok(p)) return QLORA_ERR_INVALID_ARG;
+  if (!bf16_ok(dY) || !bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B)) return QLORA_ERR_INVALID_ARG;
+  if (!bf16_opt(T) || !bf16_opt(dX) || !bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
+  if (!keep || !aligned(keep, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 16) || ws_bytes < qlora_linear_dropout_workspace_bytes(M, W->rows, W->cols, r, 1))
+    return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const NF4View v = view_of(W);
+  const int m = static_cast<int>(M);
+  const float se = drop_scale(scale, p);
+  const BwdWs L = bwd_ws(M, v.N, v.K, r);
+  char *base = static_cast<char *>(ws);
+  uint16_t *Xd = reinterpret_cast<uint16_t *>(base);
+  base += bf16_bytes(M * v.K);
+  uint16_t *Tw = reinterpret_cast<uint16_t *>(base);
+  uint16_t *G = reinterpret_cast<uint16_t *>(base + L.t);
+  void *bt = base + L.t + L.g;
+  void *pa = base + L.t + L.g + L.bt;
+  void *pb = base + L.t + L.g + L.bt + L.pa;
+  hipError_t e = hipSuccess;
+  if (dA || (dB && !T)) e = launch_dropout_apply(X, M * v.K, keep, Xd, s);
+  if (e == hipSuccess && (dX || dA)) e = launch_lora_grad_in(dY, m, v.N, B, r, se, G, bt, s);
+  if (e == hipSuccess && dX) e = launch_matmul_dx_drop(dY, m, v, G, A, r, keep, dX, s);
+  if (e == hipSuccess && dA) e = launch_lora_grad_w(Xd, G, m, v.K, r, true, dA, pa, s);
+  if (e == hipSuccess && dB) {
+    const uint16_t *Tu = T;
+    if (!Tu) {
+      e = launch_lora_down(Xd, m, v.K, A, r, se, Tw, s);
+      Tu = Tw;
+    }
+    if (e == hipSuccess) e = launch_lora_grad_w(dY, Tu, m, v.N, r, false, dB, pb, s);
+  }
+  return from_hip(e);
+}
+
 }  // extern "C"

@@ -33,6 +33,15 @@ struct NF4View {
 // Y [M, N] = X deq(W)^T + T B^T
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s);
+// ---- LoRA dropout (keep mask of the LoRA input) ------------------------------
+// n = M K elements, K % 32 == 0; keep: uint32 [M][K / 32], bit k % 32.
+hipError_t launch_dropout_mask(const uint16_t *X, int64_t n, uint64_t seed, uint32_t thresh, uint16_t *Xd,
+                               uint32_t *keep, hipStream_t s);
+hipError_t launch_dropout_apply(const uint16_t *X, int64_t n, const uint32_t *keep, uint16_t *Xd, hipStream_t s);
+// dX = dY deq(W) + (G A) * keep
+hipError_t launch_matmul_dx_drop(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
+                                 const uint16_t *A, int r, const uint32_t *keep, uint16_t *dX, hipStream_t s);
+
 // ---- LoRA products of linears sharing one input X (q/k/v, gate/up) -----------
 // Member i: R[i] (A_i for T, G_i for dA; rcols[i] columns per row), r[i],
 // scale[i], out[i]; part[i] / plane[i]: its fp32 split partials (dA only).

@@ -301,10 +301,15 @@ __device__ __forceinline__ void tile_coords(int tiles_cols, int &tr, int &tc) {
 
 // kDx = false: left = X [M, K] (contraction K), weight tile [256 n][64 k].
 // kDx = true:  left = dY [M, N] (contraction N), weight tile [64 n][256 k].
-template <bool kDx>
+// kDrop (dX only): the LoRA term is gated by the dropout keep mask of the
+// LoRA input, dX = dY deq(W) + (G A) * keep (keep: bit k % 32 of word
+// [m][k / 32]); the LoRA steps then run first, the mask zeroes their dropped
+// elements in the accumulators, and the base contraction follows.
+template <bool kDx, bool kDrop>
 __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restrict__ L, int M, NF4View w,
                                                        const uint16_t *__restrict__ Ln,
                                                        const uint16_t *__restrict__ Rn, int r,
+                                                       const uint32_t *__restrict__ keep,
                                                        uint16_t *__restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t sX0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sX1[kStageBytes];
@@ -364,6 +369,41 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A [r, K].
+  auto lora_steps = [&]() __attribute__((always_inline)) {
+    for (int j0 = 0; j0 < r; j0 += kBK) {
+      load_narrow(sX0, Ln, r, m0, M, j0);
+      if (kDx)
+        load_a_tile(sW0, Rn, r, K, j0, c0);
+      else
+        load_narrow(sW0, Rn, r, c0, N, j0);
+      __syncthreads();
+      mfma_stage<kDx>(sX0, sW0, ops, acc);
+      __syncthreads();
+    }
+  };
+  if constexpr (kDrop) {
+    lora_steps();
+    // Accumulator (i, j, e) of this lane: row 128 wm + 32 i + 8 (e / 4) +
+    // 4 (lane / 32) + e % 4, column 64 wn + 32 j + lane % 32 of the tile; the
+    // two column blocks' mask words are adjacent (K % 64 == 0).
+    const int wm = wave >> 2, wnn = wave & 3;
+    const int kw = K >> 5;
+    const int cw = (c0 + 64 * wnn) >> 5;
+    if (cw < kw) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const uint2 kb = row < M ? *reinterpret_cast<const uint2 *>(keep + static_cast<int64_t>(row) * kw + cw)
+                                   : make_uint2(0u, 0u);
+          if (!((kb.x >> (lane & 31)) & 1u)) acc[i][0][e] = 0.f;
+          if (!((kb.y >> (lane & 31)) & 1u)) acc[i][1][e] = 0.f;
+        }
+    }
+  }
 
   for (int i = tid; i < 256; i += kThreadsMM) {
     if (i < 16) sNf4[i] = u2f(cMMQ4Level[16 * w.qtype + i]);
@@ -452,17 +492,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   if (kt < KT) step(C0(), kt, b1, b0);
   mfma_rows<2, 4>(fb, acc);   // held back by the last step
 
-  // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A [r, K].
-  for (int j0 = 0; j0 < r; j0 += kBK) {
-    load_narrow(sX0, Ln, r, m0, M, j0);
-    if (kDx)
-      load_a_tile(sW0, Rn, r, K, j0, c0);
-    else
-      load_narrow(sW0, Rn, r, c0, N, j0);
-    __syncthreads();
-    mfma_stage<kDx>(sX0, sW0, ops, acc);
-    __syncthreads();
-  }
+  if constexpr (!kDrop) lora_steps();
 
   // Epilogue: the wave's 128 x 64 block as bf16 into its own 16 KB region
   // (16-byte chunks XOR-swizzled by row), then 16-byte stores guarded by the
@@ -497,14 +527,23 @@ hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const u
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s) {
   if (small_m_ok(M, r)) return launch_small_m_fwd(X, M, w, T, B, r, Y, s);
   const int tiles = ((M + kBM - 1) / kBM) * ((w.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_matmul<false>, dim3(tiles), dim3(kThreadsMM), 0, s, X, M, w, T, B, r, Y);
+  hipLaunchKernelGGL((k_matmul<false, false>), dim3(tiles), dim3(kThreadsMM), 0, s, X, M, w, T, B, r,
+                     static_cast<const uint32_t *>(nullptr), Y);
   return hipGetLastError();
 }
 
 hipError_t launch_matmul_dx(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
                             const uint16_t *A, int r, uint16_t *dX, hipStream_t s) {
   const int tiles = ((M + kBM - 1) / kBM) * ((w.K + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_matmul<true>, dim3(tiles), dim3(kThreadsMM), 0, s, dY, M, w, G, A, r, dX);
+  hipLaunchKernelGGL((k_matmul<true, false>), dim3(tiles), dim3(kThreadsMM), 0, s, dY, M, w, G, A, r,
+                     static_cast<const uint32_t *>(nullptr), dX);
+  return hipGetLastError();
+}
+
+hipError_t launch_matmul_dx_drop(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
+                                 const uint16_t *A, int r, const uint32_t *keep, uint16_t *dX, hipStream_t s) {
+  const int tiles = ((M + kBM - 1) / kBM) * ((w.K + kBN - 1) / kBN);
+  hipLaunchKernelGGL((k_matmul<true, true>), dim3(tiles), dim3(kThreadsMM), 0, s, dY, M, w, G, A, r, keep, dX);
   return hipGetLastError();
 }
 

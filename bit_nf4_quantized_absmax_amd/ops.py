@@ -279,6 +279,83 @@ def lora_dA_shared(X, Gs, outs=None, workspace=None):
     return dAs
 
 
+def dropout_mask(X, p, seed):
+    """(X_d, keep): the LoRA input with dropout p (qlora_dropout_mask); keep is
+    int32 [M, K / 32], bit k % 32 of word k / 32."""
+    M, K = X.shape
+    _need(X, torch.bfloat16, "X")
+    Xd = torch.empty_like(X)
+    keep = torch.empty(M, K // 32, dtype=torch.int32, device=X.device)
+    check(lib().qlora_dropout_mask(_ptr(X), M, K, float(p), int(seed), _ptr(Xd), _ptr(keep), _stream(X)),
+          "qlora_dropout_mask")
+    return Xd, keep
+
+
+def dropout_apply(X, keep):
+    """X_d from X and a keep mask (qlora_dropout_apply)."""
+    M, K = X.shape
+    _need(X, torch.bfloat16, "X")
+    _need(keep, torch.int32, "keep", (M, K // 32))
+    Xd = torch.empty_like(X)
+    check(lib().qlora_dropout_apply(_ptr(X), M, K, _ptr(keep), _ptr(Xd), _stream(X)), "qlora_dropout_apply")
+    return Xd
+
+
+def nf4_matmul_dx_dropout(dY, w, G, A, keep, out=None):
+    """dX = dY deq(W) + (G A) * keep (G = s_eff dY B)."""
+    M = dY.shape[0]
+    r = A.shape[0]
+    _need(dY, torch.bfloat16, "dY", (M, w.rows))
+    _need(G, torch.bfloat16, "G", (M, r))
+    _need(A, torch.bfloat16, "A", (r, w.cols))
+    _need(keep, torch.int32, "keep", (M, w.cols // 32))
+    dX = out if out is not None else torch.empty(M, w.cols, dtype=torch.bfloat16, device=dY.device)
+    st = w.struct()
+    check(lib().qlora_nf4_matmul_dx_dropout(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, _ptr(keep), _ptr(dX),
+                                            _stream(dY)), "qlora_nf4_matmul_dx_dropout")
+    return dX
+
+
+def dropout_scale(scale, p):
+    """s_eff = fl32(s / (1 - p)), the LoRA scale with inverted dropout."""
+    import numpy as np
+    return float(np.float32(float(np.float32(scale)) / (1.0 - float(np.float32(p)))))
+
+
+def linear_fwd_dropout(X, w, A, B, scale, p, seed, T_out=None, out=None, workspace=None):
+    """Forward with LoRA dropout: returns (Y, T, keep)."""
+    M, N, K, r = _lin_checks(X, w, A, B)
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    keep = torch.empty(M, K // 32, dtype=torch.int32, device=X.device)
+    ws_bytes = lib().qlora_linear_dropout_workspace_bytes(M, N, K, r, 0)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=X.device)
+    st = w.struct()
+    check(lib().qlora_linear_fwd_dropout(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), float(p),
+                                         int(seed), _ptr(Y), _ptr(T), _ptr(keep), _ptr(ws), ws_bytes, _stream(X)),
+          "qlora_linear_fwd_dropout")
+    return Y, T, keep
+
+
+def linear_bwd_dropout(dY, X, T, w, A, B, scale, p, keep, need_dX=True, need_dA=True, need_dB=True,
+                       workspace=None):
+    """Backward with LoRA dropout given the forward's keep mask: (dX, dA, dB)."""
+    M, N, K, r = _lin_checks(X, w, A, B)
+    _need(dY, torch.bfloat16, "dY", (M, N))
+    _need(keep, torch.int32, "keep", (M, K // 32))
+    dev = X.device
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev) if need_dX else None
+    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev) if need_dA else None
+    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
+    ws_bytes = lib().qlora_linear_dropout_workspace_bytes(M, N, K, r, 1)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    st = w.struct()
+    check(lib().qlora_linear_bwd_dropout(_ptr(dY), _ptr(X), _ptr(T), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
+                                         float(scale), float(p), _ptr(keep), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                         ws_bytes, _stream(X)), "qlora_linear_bwd_dropout")
+    return dX, dA, dB
+
+
 def nf4_matmul_fwd(X, w, T, B, out=None):
     """Y = X deq(W)^T + T B^T (T = scale X A^T)."""
     M = X.shape[0]

@@ -280,6 +280,48 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
                      const uint16_t *T, int64_t M, int64_t N, int64_t K, int32_t r,
                      uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- LoRA dropout on the adapter input -----------------------------------
+ * The pages' adapters drop their input with probability p (creativeworksof
+ * knowledge.com, "QLoRA: Fine-Tune 70B on One GPU", Code: lora_dropout=0.05).
+ * Keep mask: element e = m*K + k of X [M, K] is kept iff word e % 4 of
+ * Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2,
+ * 3", SC 2011) at counter (e / 4 as a 64-bit value in words 0 and 1, words 2
+ * and 3 zero) under key (seed low 32 bits, seed high 32 bits) is >=
+ * floor(p * 2^32).  The mask is stored as uint32 keep[M][K / 32], bit k % 32
+ * of word k / 32 (16-byte aligned).  Inverted dropout: the LoRA scale
+ * becomes s_eff = fl32(s / (1 - p)) (quotient in fp64); the dropped input
+ * X_d = X where kept, +0 elsewhere.  The layer with dropout:
+ *   T  = s_eff X_d A^T           Y  = X deq(W)^T + T B^T
+ *   G  = s_eff dY B              dX = dY deq(W) + (G A) * keep
+ *   dA = G^T X_d                 dB = dY^T T
+ * Rules: 0 <= p < 1 finite (else INVALID_ARG), K % 32 == 0 for the mask
+ * calls (the layer calls need K % 64 == 0 as usual). */
+
+/* X_d [M, K] and keep from X [M, K], p and seed. */
+int qlora_dropout_mask(const uint16_t *X, int64_t M, int64_t K, float p, uint64_t seed, uint16_t *X_drop,
+                       uint32_t *keep, void *stream);
+/* X_d from X and an existing keep mask (the backward pass). */
+int qlora_dropout_apply(const uint16_t *X, int64_t M, int64_t K, const uint32_t *keep, uint16_t *X_drop,
+                        void *stream);
+/* dX [M, K] = dY deq(W) + (G A) * keep  (G = s_eff dY B, given). */
+int qlora_nf4_matmul_dx_dropout(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W, const uint16_t *G,
+                                const uint16_t *A, int32_t r, const uint32_t *keep, uint16_t *dX, void *stream);
+/* Workspace of the dropout layer calls: X_d plus the forward's T or the
+ * backward's workspace (is_bwd). */
+size_t qlora_linear_dropout_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd);
+/* Forward with dropout; writes keep_out [M][K / 32] for the backward pass and
+ * T to T_out (nullable: workspace). */
+int qlora_linear_fwd_dropout(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *A,
+                             const uint16_t *B, int32_t r, float scale, float p, uint64_t seed, uint16_t *Y,
+                             uint16_t *T_out, uint32_t *keep_out, void *ws, size_t ws_bytes, void *stream);
+/* Backward with dropout, given the forward's keep mask; T as written by the
+ * forward (NULL: recomputed from X_d); dX, dA, dB nullable as in
+ * qlora_linear_bwd. */
+int qlora_linear_bwd_dropout(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,
+                             const qlora_nf4_weight *W, const uint16_t *A, const uint16_t *B, int32_t r, float scale,
+                             float p, const uint32_t *keep, uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws,
+                             size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

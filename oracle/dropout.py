@@ -67,18 +67,29 @@ def effective_scale(scale, p):
     return np.float32(float(np.float32(scale)) / (1.0 - float(p)))
 
 
-def keep_mask(M, K, p, seed):
-    """bool [M, K]: which elements of the LoRA input survive."""
-    n = M * K
-    e = np.arange(n, dtype=np.uint64)
-    blocks = np.arange((n + 3) // 4, dtype=np.uint64)
-    ctr = np.zeros((len(blocks), 4), np.uint32)
+def _keep_elements(e, p, seed):
+    """Keep flags of flat element indices e (uint64)."""
+    e = np.asarray(e, dtype=np.uint64)
+    blocks = e // np.uint64(4)
+    ctr = np.zeros((len(e), 4), np.uint32)
     ctr[:, 0] = (blocks & MASK32).astype(np.uint32)
     ctr[:, 1] = (blocks >> np.uint64(32)).astype(np.uint32)
     seed = int(seed)
     words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
-    w = words[(e // np.uint64(4)).astype(np.int64), (e % np.uint64(4)).astype(np.int64)]
-    return (w.astype(np.uint64) >= np.uint64(threshold(p))).reshape(M, K)
+    w = words[np.arange(len(e)), (e % np.uint64(4)).astype(np.int64)]
+    return w.astype(np.uint64) >= np.uint64(threshold(p))
+
+
+def keep_mask(M, K, p, seed):
+    """bool [M, K]: which elements of the LoRA input survive."""
+    return _keep_elements(np.arange(M * K, dtype=np.uint64), p, seed).reshape(M, K)
+
+
+def keep_mask_rows(rows, K, p, seed):
+    """The rows `rows` of keep_mask(M, K, p, seed), for any M > max(rows)."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    e = rows[:, None] * np.uint64(K) + np.arange(K, dtype=np.uint64)[None, :]
+    return _keep_elements(e.reshape(-1), p, seed).reshape(len(rows), K)
 
 
 def pack_bits(keep):

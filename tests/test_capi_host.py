@@ -139,6 +139,24 @@ def test_validation_rejects_before_launch():
     assert L.qlora_lora_dA_shared(P, 8, 64, 3, PA, R3, PA, None, 0, None) == WS
     assert L.qlora_lora_dA_shared(P, 8, 64, 3, PA, R3, None, P, 1 << 20, None) == INVALID
     assert L.qlora_lora_dA_shared(P, 0, 64, 3, PA, R3, PA, P, 1 << 20, None) == OK
+    # dropout: p range, K % 32, keep pointer, workspace, M = 0
+    assert L.qlora_dropout_mask(P, 8, 64, 1.0, 1, P, P, None) == INVALID
+    assert L.qlora_dropout_mask(P, 8, 64, -0.1, 1, P, P, None) == INVALID
+    assert L.qlora_dropout_mask(P, 8, 64, float("nan"), 1, P, P, None) == INVALID
+    assert L.qlora_dropout_mask(P, 8, 48, 0.1, 1, P, P, None) == SHAPE
+    assert L.qlora_dropout_mask(P, 8, 64, 0.1, 1, P, None, None) == INVALID
+    assert L.qlora_dropout_mask(P, 0, 64, 0.1, 1, P, P, None) == OK
+    assert L.qlora_dropout_apply(P, 8, 64, None, P, None) == INVALID
+    assert L.qlora_nf4_matmul_dx_dropout(P, 8, ctypes.byref(w), P, P, 8, None, P, None) == INVALID
+    assert L.qlora_linear_dropout_workspace_bytes(8192, 4096, 4096, 64, 0) >= 8192 * 4096 * 2
+    assert L.qlora_linear_dropout_workspace_bytes(8192, 4096, 4000, 64, 0) == 0
+    assert L.qlora_linear_fwd_dropout(P, 8, ctypes.byref(w), P, P, 8, 1.0, 0.1, 1, P, None, P, None, 0, None) == WS
+    assert L.qlora_linear_fwd_dropout(P, 8, ctypes.byref(w), P, P, 8, 1.0, 1.5, 1, P, None, P, P, 1 << 20, None) \
+        == INVALID
+    assert L.qlora_linear_bwd_dropout(P, P, None, 8, ctypes.byref(w), P, P, 8, 1.0, 0.1, None, P, P, P, P, 1 << 30,
+                                      None) == INVALID
+    assert L.qlora_linear_bwd_dropout(P, P, None, 0, ctypes.byref(w), P, P, 8, 1.0, 0.1, P, P, P, P, P, 1 << 30,
+                                      None) == OK
     # 16-bit input quantize: input type outside the enum, null or misaligned input, workspace
     assert L.qlora_quantize_nf4_16(P, 0, ctypes.byref(w), P, 1 << 20, None) == INVALID
     assert L.qlora_quantize_nf4_16(P, 3, ctypes.byref(w), P, 1 << 20, None) == INVALID

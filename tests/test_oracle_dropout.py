@@ -51,6 +51,12 @@ def test_mask_uses_word_e_mod_4_of_block_e_div_4():
     assert np.array_equal(keep, words.reshape(-1) >= 2 ** 31)
 
 
+def test_row_subset_matches_the_full_mask():
+    full = od.keep_mask(40, 96, 0.2, 77)
+    rows = np.array([0, 7, 39])
+    assert np.array_equal(od.keep_mask_rows(rows, 96, 0.2, 77), full[rows])
+
+
 def test_bits_round_trip():
     rng = np.random.default_rng(3)
     keep = rng.random((5, 70)) < 0.9
