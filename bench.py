@@ -571,7 +571,7 @@ def main():
     dom_key = max(kern, key=lambda k: kern[k]["total_ms"])
     dom = kern[dom_key]
     achieved = dom["flops_per_launch"] / (dom["avg_us"] * 1e-6) / 1e12
-    dom_kernel = "qlora::k_matmul<false>" if dom_key == "fwd" else "qlora::k_matmul<true>"
+    dom_kernel = "qlora::k_matmul<false, false>" if dom_key == "fwd" else "qlora::k_matmul<true, false>"
     roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=recorded_traffic(dom_kernel),
                     traffic_unit="HBM bytes per launch (PMC FETCH_SIZE/WRITE_SIZE, copy-scaled)",
