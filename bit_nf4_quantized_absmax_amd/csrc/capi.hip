@@ -323,14 +323,11 @@ static bool group_one_type(int count, const qlora_linear_desc *d) {
 
 size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *d, int64_t M) {
   if (count < 1 || count > kSmMaxGroup || !d) return 0;
-  size_t total = 0, most = 0;
+  size_t total = 0;
   for (int i = 0; i < count; ++i) {
     if (!d[i].W || check_linear_shape(M, d[i].W, d[i].r, d[i].scale)) return 0;
-    const size_t b = fwd_ws(M, d[i].W->rows, d[i].W->cols, d[i].r);
-    total += b;
-    most = std::max(most, b);
+    total += fwd_ws(M, d[i].W->rows, d[i].W->cols, d[i].r);
   }
-  (void)most;
   return total;   // decode regime: every linear's partials; larger M: every T at once
 }
 

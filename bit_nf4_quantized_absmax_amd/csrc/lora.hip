@@ -10,6 +10,10 @@
 //   k_lora_tn   dA = G^T X   [r, K]   contraction over M (both read transposed)
 //               dB = dY^T T  [N, r]
 //   k_sum_partials   fixed-order sum of the M-split partials of k_lora_tn
+//   k_lora_nt_shared, k_lora_tn_shared   T and dA of several linears that
+//               read the same X (q / k / v, gate / up), one launch each; the
+//               tiles are those of k_lora_nt / k_lora_tn, so the results are
+//               bit-identical
 // G and T carry the scale, which is applied once, in fp32, before T and G are
 // rounded to bf16.  These are streaming products: each reads its wide operand
 // (X or dY) once from HBM.
