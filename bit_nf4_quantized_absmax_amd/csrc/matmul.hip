@@ -136,7 +136,7 @@ __device__ __forceinline__ void load_block(WBlock &b, const NF4View &w, int n, i
 __device__ __forceinline__ uint32_t nf4_lo4(uint32_t w) { return (w << 2) & 0x3C3C3C3Cu; }
 __device__ __forceinline__ uint32_t nf4_hi4(uint32_t w) { return (w >> 2) & 0x3C3C3C3Cu; }
 __device__ __forceinline__ float nf4_level(const float *nf4, uint32_t off4, int b) {
-  return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(nf4) + ((off4 >> (8 * b)) & 0xffu));
+  return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(nf4) + __builtin_amdgcn_ubfe(off4, 8 * b, 8));
 }
 
 // Chunk c (codes 8 c .. 8 c + 7 of the half block): the 8 fp32 levels, then
@@ -144,7 +144,8 @@ __device__ __forceinline__ float nf4_level(const float *nf4, uint32_t off4, int 
 // while before their products are needed.
 __device__ __forceinline__ void chunk_levels(float (&lv)[8], const WBlock &b, int c, const float *nf4) {
   const uint32_t words[4] = {b.p.x, b.p.y, b.p.z, b.p.w};
-  const uint32_t lo4 = nf4_lo4(words[c]), hi4 = nf4_hi4(words[c]);
+  uint32_t lo4 = nf4_lo4(words[c]), hi4 = nf4_hi4(words[c]);
+  asm volatile("" : "+v"(lo4), "+v"(hi4));   // keep the byte offsets: one extract per code
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     lv[2 * q] = nf4_level(nf4, lo4, q);
