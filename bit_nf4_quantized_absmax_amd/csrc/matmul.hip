@@ -437,9 +437,10 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   //  * head: operands of sub-step 0, the block's absmax code and the levels
   //    of chunk 0 are read while the last four MFMAs of the previous step
   //    (held back from before the barrier, their operands in registers) run;
-  //  * sub-step s: two MFMAs, then the levels of chunk s and the operands of
-  //    sub-step s + 1 are read, two more MFMAs, then chunk s is scaled and
-  //    written while the last four MFMAs run.
+  //  * sub-step s: two MFMAs, then the levels of chunk s + 1 (one sub-step
+  //    ahead, so their LDS latency is hidden) and the operands of sub-step
+  //    s + 1 are read, two more MFMAs, then chunk s is scaled and written
+  //    while the last four MFMAs run.
   Frag fa, fb;   // operands of the even / odd sub-steps
 #pragma unroll
   for (int i = 0; i < 4; ++i) fb.a[i] = bf16x8_t{};
@@ -451,10 +452,10 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
     const uint8_t *wr = CUR ? sW1 : sW0;
     uint8_t *xn = CUR ? sX0 : sX1;
     uint8_t *wn = CUR ? sW0 : sW1;
-    float lv[8];
+    float lv[2][8];   // levels of chunk s in lv[s & 1], read one sub-step ahead
     load_frag<kDx>(fa, xs, wr, ops, 0);
     const float t8 = sT8[bn.code];
-    chunk_levels(lv, bn, 0, sNf4);
+    chunk_levels(lv[0], bn, 0, sNf4);
     // First use of the whole block of kt + 1 before any newer load is issued:
     // the wait for it then covers only loads issued a step ago.
     asm volatile("" ::"v"(bn.p.x), "v"(bn.p.y), "v"(bn.p.z), "v"(bn.p.w), "v"(bn.c2));
@@ -473,11 +474,11 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
       Frag &nxt = (s & 1) ? fa : fb;
       mfma_rows<0, 1>(cur, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (s > 0) chunk_levels(lv, bn, s, sNf4);
+      if (s < 3) chunk_levels(lv[(s + 1) & 1], bn, s + 1, sNf4);
       if (s < 3) load_frag<kDx>(nxt, xs, wr, ops, s + 1);
       mfma_rows<1, 2>(cur, acc);
       __builtin_amdgcn_sched_barrier(0);
-      put_chunk(wn, s, scale_chunk(lv, chat));
+      put_chunk(wn, s, scale_chunk(lv[s & 1], chat));
       if (s < 3) mfma_rows<2, 4>(cur, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
