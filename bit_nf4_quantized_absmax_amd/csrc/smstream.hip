@@ -172,11 +172,14 @@ __global__ __launch_bounds__(256) void k_ss_finish(SmGroup grp) {
 // chunk.  Each wait-and-barrier round then moves kPT x 8 KB of weights (the
 // per-round cost of the LDS DMA stream is fixed, so larger rounds stream
 // faster), within the 160 KB of LDS.
+// From three token tiles up, X takes two stages (prefetched one unit ahead)
+// instead of three, which leaves room for more weight tiles per unit: each X
+// chunk then serves 2-3 row tiles instead of 1-2.
 template <int kMB>
 constexpr int ss_pt() {
-  return kMB == 1 ? 4 : (kMB == 2 ? 3 : (kMB == 3 ? 2 : 1));
+  return kMB == 1 ? 4 : (kMB == 2 ? 3 : (kMB == 3 ? 3 : 2));
 }
-int ss_pt_of(int kmb) { return kmb == 1 ? 4 : (kmb == 2 ? 3 : (kmb == 3 ? 2 : 1)); }
+int ss_pt_of(int kmb) { return kmb == 1 ? 4 : (kmb == 2 ? 3 : (kmb == 3 ? 3 : 2)); }
 
 // Per-linear values the DMA iterators need, reloaded when they cross into the
 // next linear.
@@ -327,17 +330,20 @@ __device__ __forceinline__ void ss_finish_rows(const SmLinear &L, int M, int gro
 template <int kMB>
 __global__ __launch_bounds__(kSsThreads) void k_ss_stream(SmGroup grp) {
   constexpr int kPT = ss_pt<kMB>();
-  constexpr int kXS = 3;                        // X and weight stages: both two units ahead
-  constexpr int kWS = 3;
+  constexpr int kXS = kMB >= 3 ? 2 : 3;         // X stages: X one or two units ahead
+  constexpr int kWS = 3;                        // weight stages: two units ahead
   constexpr int kXStage = kMB * 16 * 512;
   constexpr int kWStage = kPT * kSsWStage;
   constexpr int kPiece = 2 * 2 * kMB * 4 * 64;  // floats: [rh][rg][mb][e][lane]
   // DMA instructions per wave and unit: kPT (packed weights), waves
   // 0 .. 2 kPT - 1 one gather (codes of tile w, or group scales of tile
-  // w - kPT), then kMB (X).  Unit q issues the weights and X of q + 2; at its
-  // end everything up to unit q + 1 must have landed.
-  constexpr int kAfter = kPT + kMB;
-  constexpr int kAfterG = kPT + 1 + kMB;
+  // w - kPT), and kMB (X).  At the end of unit q everything up to unit q + 1
+  // must have landed.  Three X stages: unit q issues the weights, then the X,
+  // of q + 2, and both may stay in flight.  Two X stages: unit q issues the X
+  // of q + 1, then the weights of q + 2; only those weights may stay in
+  // flight (the counter retires DMAs in issue order).
+  constexpr int kAfter = kXS == 3 ? kPT + kMB : kPT;
+  constexpr int kAfterG = kAfter + 1;
   static_assert(2 * kPiece * 4 <= kXStage, "tile sums fit in an X stage");
   __shared__ __attribute__((aligned(16))) uint8_t sX[kXS * kXStage];
   __shared__ __attribute__((aligned(16))) uint8_t sW[kWS * kWStage];
@@ -417,17 +423,35 @@ __global__ __launch_bounds__(kSsThreads) void k_ss_stream(SmGroup grp) {
   SsPos pc = ss_locate<kPT>(grp, u0);          // compute position
   SsPos px = pc, pw = pc;                     // DMA positions (X, weights)
   int qx = 0, qw = 0;
-  auto issue_next = [&]() __attribute__((always_inline)) {
+  auto issue_w = [&]() __attribute__((always_inline)) {
     dma_w(qw, pw);
-    dma_x(qx, px);
     if (qw + 1 < nq) ss_advance<kPT>(grp, pw);
     ++qw;
+  };
+  auto issue_x = [&]() __attribute__((always_inline)) {
+    dma_x(qx, px);
     if (qx + 1 < nq) ss_advance<kPT>(grp, px);
     ++qx;
   };
-  // Issue order W(0) X(0) W(1) X(1): the steady-state order.
-  issue_next();
-  issue_next();
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if constexpr (kXS == 3) {
+      issue_w();
+      issue_x();
+    } else {
+      issue_x();
+      issue_w();
+    }
+  };
+  // Prologue in the steady-state order: W(0) X(0) W(1) X(1) with three X
+  // stages, X(0) W(0) W(1) with two.
+  if constexpr (kXS == 3) {
+    issue_next();
+    issue_next();
+  } else {
+    issue_x();
+    issue_w();
+    issue_w();
+  }
   round_end();
 
   f32x4_t acc[kPT][2][kMB];
@@ -442,7 +466,7 @@ __global__ __launch_bounds__(kSsThreads) void k_ss_stream(SmGroup grp) {
   int wfirst = ss_wg_of(grp.cost0[pc.li], G, U);
 
   for (int q = 0; q < nq; ++q) {
-    issue_next();                               // weights and X of unit q + 2
+    issue_next();                               // weights of unit q + 2, X of q + 2 or q + 1
 
     const uint8_t *xs = sX + (q % kXS) * kXStage;
     const uint8_t *ws0 = sW + (q % kWS) * kWStage;
