@@ -25,13 +25,14 @@ __constant__ uint32_t cT8Thresh[255] = {QLORA_T8_THRESH_BITS};
 constexpr int kTreeChunk = 2048;   // elements reduced by one workgroup of k_tree_sum
 constexpr int kThreads = 256;
 
-// Nearest level of the 4-bit table `qtype`, ties to the lower code: number of
-// thresholds below x.
-__device__ __forceinline__ uint32_t q4_code(float x, int qtype) {
-  const uint32_t *th = cQ4Thresh + 15 * qtype;
-  uint32_t q = 0;
-#pragma unroll
-  for (int i = 0; i < 15; ++i) q += (x > u2f(th[i])) ? 1u : 0u;
+// Nearest level of a 4-bit table, ties to the lower code: the number of its 15
+// ascending thresholds (th, in LDS) strictly below x, by a 4-step binary
+// search (equal thresholds, as FP4's two zero levels give, are counted alike).
+__device__ __forceinline__ uint32_t q4_code(float x, const float *th) {
+  uint32_t q = (x > th[7]) ? 8u : 0u;
+  q += (x > th[q + 3]) ? 4u : 0u;
+  q += (x > th[q + 1]) ? 2u : 0u;
+  q += (x > th[q]) ? 1u : 0u;
   return q;
 }
 
@@ -56,6 +57,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restric
                                                            int qtype, uint8_t *__restrict__ packed,
                                                            float *__restrict__ absmax) {
   const uint32_t zero = static_cast<uint32_t>(q4_zero_code(qtype));
+  __shared__ float sTh[16];
+  if (threadIdx.x < 15) sTh[threadIdx.x] = u2f(cQ4Thresh[15 * qtype + threadIdx.x]);
+  __syncthreads();
   const int64_t nchunks = ((n + kBlock - 1) / kBlock) * 16;  // 4-element chunks, whole blocks
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nchunks; c += stride) {
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restric
     uint32_t q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      q[i] = (a > 0.0f) ? q4_code(w[i] / a, qtype) : zero;
+      q[i] = (a > 0.0f) ? q4_code(w[i] / a, sTh) : zero;
       if (e + i >= n) q[i] = 0u;
     }
     const uint32_t b0 = q[0] | (q[1] << 4), b1 = q[2] | (q[3] << 4);
