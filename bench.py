@@ -22,12 +22,19 @@ Also reported on the same JSON line:
                 median and minimum per layer), algorithmic HBM GB/s:
                 7 single-linear calls per layer and one grouped call
   quantize      quantize throughput on the 7 weights (algorithmic GB/s)
+  dequantize    standalone dequantization to bf16 of the 7 weights over 4
+                weight sets, from a HIP graph (algorithmic GB/s, HBM fraction)
+  small_config  the 1024 x 1024, M = 128, r = 8 parity configuration:
+                quantize, forward, backward (launch-bound, for reference)
   q4_types      NF4 / FP4 / Int4 level tables on a 4096 x 4096 weight:
                 reconstruction error, quantize from fp32 and bf16, forward
   shared_input  LoRA products of q / k / v and gate / up (one X): separate
                 launches against one shared-input launch
   dropout       the 7B step with LoRA dropout p = 0.05 against without, and
                 the keep-mask kernel
+  llama33b_layer, llama65b
+                fwd + bwd of one 33B / 65B layer; the 65B model's 80 layers
+                quantized, with the codec oracle timed on one of its weights
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
                        [--copy-probe-mib MiB] [--small-m-only [--small-m-eager]]
@@ -176,7 +183,18 @@ def cpu_baseline(cfg, tokens):
         olin.linear_bwd(d["dY"], d["X"], wt, d["A"], d["B"], cfg.scale)
         total_s += time.perf_counter() - t0
         total_flops += linear_flops(tokens, d["N"], d["K"], d["r"])
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = None
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
     return dict(value=total_flops / total_s / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                affinity_cpus=affinity, cpu_model=cpu_model,
                 sample="fp64 NumPy oracle fwd+bwd of all 7 linears (dequantize + products) on %d of the 8192 "
                        "tokens, %.1f s; rate = algorithmic FLOP / time" % (tokens, total_s))
 
@@ -478,6 +496,112 @@ def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3):
                 TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1), frac_bf16_peak=round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4))
 
 
+def dequantize_bench(q, torch, workloads, cfg, dev, reps=20):
+    """Standalone dequantization (packed codes + constants -> bf16) of the 7
+    weights of a layer, over 4 weight sets (> the 256 MB Infinity Cache),
+    captured once in a HIP graph with preallocated outputs and replayed.
+    Algorithmic bytes per parameter: 1/2 (codes) + 1/64 (constant codes) +
+    4/16384 (group scales) read, 2 (bf16) written."""
+    import ctypes
+    sets, outs = [], []
+    for si in range(4):
+        ws = []
+        for li, lin in enumerate(cfg.linears):
+            W = workloads.device_normal((lin.out_features, lin.in_features), workloads.W_STD, 97000 + 100 * si + li, dev)
+            ws.append(q.NF4Weight.quantize(W))
+            del W
+        sets.append([w.struct() for w in ws] + [ws])
+        outs.append([torch.empty(l.out_features, l.in_features, dtype=torch.bfloat16, device=dev) for l in cfg.linears])
+    lib = q.lib()
+
+    def run(stream):
+        for si in range(4):
+            for st, o in zip(sets[si][:-1], outs[si]):
+                rc = lib.qlora_dequantize_nf4(ctypes.byref(st), o.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("qlora_dequantize_nf4 failed: %d" % rc)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run(stream)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record()
+    for i in range(reps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / 4 for i in range(reps))
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / (4 * reps)
+    params = sum(l.out_features * l.in_features for l in cfg.linears)
+    nbytes = params * (0.5 + 1 / 64 + 4 / 16384 + 2)
+    del graph, sets, outs
+    torch.cuda.empty_cache()
+    return dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
+                params=int(params), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), launches_per_layer=len(cfg.linears))
+
+
+def small_config_bench(q, torch, workloads, cfg, dev, reps=20):
+    """The small parity configuration (one linear): quantize, forward and
+    backward, eager calls; launch-bound at this size, reported for reference."""
+    lin = cfg.linears[0]
+    N, K, M, r = lin.out_features, lin.in_features, cfg.tokens, cfg.rank
+    W = workloads.device_normal((N, K), workloads.W_STD, 98000, dev)
+    bf = torch.bfloat16
+    X = workloads.device_normal((M, K), 1.0, 98001, dev, bf)
+    A = workloads.device_normal((r, K), workloads.LORA_STD, 98002, dev, bf)
+    B = workloads.device_normal((N, r), workloads.LORA_STD, 98003, dev, bf)
+    dY = workloads.device_normal((M, N), 1.0, 98004, dev, bf)
+    w = q.NF4Weight.quantize(W)
+    Y, T = q.linear_fwd(X, w, A, B, cfg.scale)
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return round(sorted(ts)[reps // 2], 2)
+
+    return dict(workload=cfg.name, quantize_us=med(lambda: q.NF4Weight.quantize(W)),
+                fwd_us=med(lambda: q.linear_fwd(X, w, A, B, cfg.scale)),
+                bwd_us=med(lambda: q.linear_bwd(dY, X, T, w, A, B, cfg.scale)),
+                fwd_bwd_flops=linear_flops(M, N, K, r),
+                note="median of %d eager calls each (workspaces and outputs allocated by the binding)" % reps)
+
+
+def codec_cpu_baseline(workloads, cfg):
+    """The codec oracle (single-threaded NumPy) on one weight of the largest
+    shape of `cfg` (drawn on the host, not timed), extrapolated to all of
+    its layers by parameter count."""
+    from oracle import nf4
+    lin = max(cfg.linears, key=lambda l: l.out_features * l.in_features)
+    W = workloads.weight((lin.out_features, lin.in_features), 99000)
+    t0 = time.perf_counter()
+    nf4.quantize(W)
+    sec = time.perf_counter() - t0
+    params = W.size
+    total = cfg.layers * sum(l.out_features * l.in_features for l in cfg.linears)
+    return dict(kind="oracle", cores=1, params_per_s=round(params / sec, 1),
+                GBps=round(params * (4 + 0.5 + 1 / 64 + 4 / 16384) / sec / 1e9, 3),
+                extrapolated_ms_all_layers=round(total / (params / sec) * 1e3, 1),
+                sample="oracle quantize of one %s weight (%d x %d, %.1f s), extrapolated x %d layers by parameter count"
+                       % (lin.name, lin.out_features, lin.in_features, sec, cfg.layers))
+
+
 def model_quantize_bench(q, torch, workloads, cfg, dev):
     """Quantize every layer of a multi-layer config, weights drawn on the device
     layer by layer (the draws are not timed)."""
@@ -589,6 +713,10 @@ def main():
         extras["small_m"] = small_m_bench(q, torch, workloads, workloads.CONFIGS[2], dev)
         log("quantize")
         extras["quantize"] = quantize_bench(q, torch, workloads, cfg, dev)
+        log("dequantize")
+        extras["dequantize"] = dequantize_bench(q, torch, workloads, cfg, dev)
+        log("small parity configuration")
+        extras["small_config"] = small_config_bench(q, torch, workloads, workloads.CONFIGS[0], dev)
         log("4-bit types")
         extras["q4_types"] = q4_types_bench(q, torch, workloads, dev)
         log("shared-input LoRA products")
@@ -602,6 +730,9 @@ def main():
         c4 = workloads.CONFIGS[4]
         extras["llama65b"] = dict(quantize=model_quantize_bench(q, torch, workloads, c4, dev),
                                   layer=layer_bench(q, torch, workloads, c4, dev, c4.tokens))
+        if not args.no_cpu:
+            log("codec oracle baseline (one 65B weight)")
+            extras["llama65b"]["quantize"]["cpu_baseline"] = codec_cpu_baseline(workloads, c4)
 
     cpu = None
     if not args.no_cpu:
