@@ -183,47 +183,69 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: each thread expands 8 consecutive elements (4 packed bytes) into
-// one 16-byte store of bf16.  All 8 share one block constant (8 | 64).
+// Dequantize: a thread expands kDqU chunks of 8 consecutive elements (4
+// packed bytes -> one 16-byte store of bf16; the 8 share one block constant,
+// 8 | 64).  Chunk u of a thread lies kThreads chunks after chunk u - 1, so
+// each load and store instruction is contiguous across the workgroup; all
+// loads of the kDqU chunks are issued before the first is used.  Levels are
+// read in pairs, one LDS entry per packed byte.  Codes are read once and the
+// output is written once: both go through non-temporal (streaming) accesses.
 // ---------------------------------------------------------------------------
+constexpr int kDqU = 8;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict__ packed,
                                                       const uint8_t *__restrict__ code8,
                                                       const float *__restrict__ c2,
                                                       const float *__restrict__ mean_p, int64_t n, int qtype,
                                                       uint16_t *__restrict__ out) {
-  __shared__ float lut[16];
+  __shared__ float2 pairs[256];   // byte -> (level of its low nibble, level of its high nibble)
   __shared__ float t8[256];
-  if (threadIdx.x < 16) lut[threadIdx.x] = u2f(cQ4Level[16 * qtype + threadIdx.x]);
-  for (int i = threadIdx.x; i < 256; i += kThreads) t8[i] = u2f(cT8Level[i]);
+  for (int i = threadIdx.x; i < 256; i += kThreads) {
+    pairs[i] = make_float2(u2f(cQ4Level[16 * qtype + (i & 15)]), u2f(cQ4Level[16 * qtype + (i >> 4)]));
+    t8[i] = u2f(cT8Level[i]);
+  }
   __syncthreads();
   const float mean = mean_p[0];
   const int64_t nchunks = (n + 7) / 8;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    const int64_t e = c * 8;
-    const int64_t b = e >> 6;
-    const float chat = decode_absmax(t8[code8[b]], c2[b >> 8], mean);
-    const bool full = (e + 7 < n);
-    uint32_t p;
-    if (full) {
-      p = *reinterpret_cast<const uint32_t *>(packed + (e >> 1));
-    } else {
-      p = 0;
-      for (int i = 0; i < 4; ++i)
-        if (e + 2 * i < n) p |= static_cast<uint32_t>(packed[(e >> 1) + i]) << (8 * i);
-    }
-    uint32_t o[4];
+  const int64_t span = static_cast<int64_t>(kThreads) * kDqU;
+  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x; c0 < nchunks;
+       c0 += static_cast<int64_t>(gridDim.x) * span) {
+    uint32_t p[kDqU], cc[kDqU];
+    float sc[kDqU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = lut[(p >> (8 * i)) & 15u] * chat;
-      const float hi = lut[(p >> (8 * i + 4)) & 15u] * chat;
-      o[i] = pack_bf16x2(lo, hi);
+    for (int u = 0; u < kDqU; ++u) {
+      const int64_t c = min(c0 + u * kThreads, nchunks - 1);   // past the end: a repeated load, never used
+      const int64_t e = c * 8, b = e >> 6;
+      cc[u] = code8[b];
+      sc[u] = c2[b >> 8];
+      if (e + 7 < n) {
+        p[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(packed + (e >> 1)));
+      } else {
+        p[u] = 0;
+        for (int i = 0; i < 4; ++i)
+          if (e + 2 * i < n) p[u] |= static_cast<uint32_t>(packed[(e >> 1) + i]) << (8 * i);
+      }
     }
-    if (full) {
-      *reinterpret_cast<uint4 *>(out + e) = make_uint4(o[0], o[1], o[2], o[3]);
-    } else {
-      for (int i = 0; i < 8; ++i)
-        if (e + i < n) out[e + i] = static_cast<uint16_t>(o[i >> 1] >> (16 * (i & 1)));
+#pragma unroll
+    for (int u = 0; u < kDqU; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      if (c >= nchunks) break;
+      const int64_t e = c * 8;
+      const float chat = decode_absmax(t8[cc[u]], sc[u], mean);
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 lv = pairs[(p[u] >> (8 * i)) & 255u];
+        o[i] = pack_bf16x2(lv.x * chat, lv.y * chat);
+      }
+      if (e + 7 < n) {
+        const u32x4_t v = {o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(out + e));
+      } else {
+        for (int i = 0; i < 8; ++i)
+          if (e + i < n) out[e + i] = static_cast<uint16_t>(o[i >> 1] >> (16 * (i & 1)));
+      }
     }
   }
 }
@@ -283,7 +305,7 @@ hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uin
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
                              const float *mean, int64_t n, int qtype, uint16_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(k_dequant, dim3(grid_for((n + 7) / 8, kThreads, 16384)), dim3(kThreads), 0, s, packed,
+  hipLaunchKernelGGL(k_dequant, dim3(grid_for((n + 7) / 8, kThreads * kDqU, 16384)), dim3(kThreads), 0, s, packed,
                      code8, c2, mean, n, qtype, out);
   return hipGetLastError();
 }
