@@ -52,6 +52,31 @@ __device__ __forceinline__ float widen(const void *W, int64_t i) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
+constexpr int kQU = 2;   // 4-element chunks per thread per pass of k_quant_blocks
+
+template <int kIn>
+__device__ __forceinline__ void load_chunk(const void *W, int64_t e, int64_t n, float w[4]) {
+  if (e + 3 < n && kIn == 0) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(static_cast<const float *>(W) + e));
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if (e + 3 < n) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(W) + e));
+    const uint32_t hs[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = kIn == 1 ? u2f(hs[i] << 16)
+                      : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hs[i])));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (e + i < n) ? widen<kIn>(W, e + i) : 0.0f;
+  }
+}
+
+// A thread takes kQU chunks kThreads apart (a 16-lane block group stays
+// within one block) and loads all of them before coding the first; W is read
+// once, through streaming loads.
 template <int kIn>
 __global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restrict__ W, int64_t n,
                                                            int qtype, uint8_t *__restrict__ packed,
@@ -61,44 +86,48 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restric
   if (threadIdx.x < 15) sTh[threadIdx.x] = u2f(cQ4Thresh[15 * qtype + threadIdx.x]);
   __syncthreads();
   const int64_t nchunks = ((n + kBlock - 1) / kBlock) * 16;  // 4-element chunks, whole blocks
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    const int64_t e = c * 4;
-    float w[4];
-    const bool full = (e + 3 < n);
-    if (full && kIn == 0) {
-      const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(W) + e);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else if (full) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(W) + e);
-      const uint32_t hs[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+  const int64_t span = static_cast<int64_t>(kThreads) * kQU;
+  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x; c0 < nchunks;
+       c0 += static_cast<int64_t>(gridDim.x) * span) {
+    float w[kQU][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = kIn == 1 ? u2f(hs[i] << 16)
-                        : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hs[i])));
-    } else {
+    for (int u = 0; u < kQU; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      if (c < nchunks) {
+        load_chunk<kIn>(W, c * 4, n, w[u]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (e + i < n) ? widen<kIn>(W, e + i) : 0.0f;
+        for (int i = 0; i < 4; ++i) w[u][i] = 0.0f;
+      }
     }
-    float a = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
+    for (int u = 0; u < kQU; ++u) {
+      // nchunks is a multiple of 16 and a block's 16 lanes share c >> 4, so
+      // a block group is wholly in range or wholly out.
+      const int64_t c = c0 + u * kThreads;
+      if (c >= nchunks) break;
+      const int64_t e = c * 4;
+      const bool full = (e + 3 < n);
+      float a = fmaxf(fmaxf(fabsf(w[u][0]), fabsf(w[u][1])), fmaxf(fabsf(w[u][2]), fabsf(w[u][3])));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
 
-    uint32_t q[4];
+      uint32_t q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      q[i] = (a > 0.0f) ? q4_code(w[i] / a, sTh) : zero;
-      if (e + i >= n) q[i] = 0u;
+      for (int i = 0; i < 4; ++i) {
+        q[i] = (a > 0.0f) ? q4_code(w[u][i] / a, sTh) : zero;
+        if (e + i >= n) q[i] = 0u;
+      }
+      const uint32_t b0 = q[0] | (q[1] << 4), b1 = q[2] | (q[3] << 4);
+      uint8_t *dst = packed + (e >> 1);
+      if (full) {
+        *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(b0 | (b1 << 8));
+      } else {
+        if (e < n) dst[0] = static_cast<uint8_t>(b0);
+        if (e + 2 < n) dst[1] = static_cast<uint8_t>(b1);
+      }
+      if ((threadIdx.x & 15) == 0) absmax[c >> 4] = a;
     }
-    const uint32_t b0 = q[0] | (q[1] << 4), b1 = q[2] | (q[3] << 4);
-    uint8_t *dst = packed + (e >> 1);
-    if (full) {
-      *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(b0 | (b1 << 8));
-    } else {
-      if (e < n) dst[0] = static_cast<uint8_t>(b0);
-      if (e + 2 < n) dst[1] = static_cast<uint8_t>(b1);
-    }
-    if ((threadIdx.x & 15) == 0) absmax[c >> 4] = a;
   }
 }
 
@@ -279,7 +308,7 @@ hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uin
   double *buf0 = reinterpret_cast<double *>(static_cast<char *>(ws) + a);
   double *buf1 = buf0 + tree_partials(nb);
 
-  const dim3 g1(grid_for(nb * 16, kThreads, 16384));
+  const dim3 g1(grid_for(nb * 16, kThreads * kQU, 16384));
   if (in_type == 1)
     hipLaunchKernelGGL(k_quant_blocks<1>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
   else if (in_type == 2)
