@@ -116,3 +116,12 @@ def test_quantize_is_deterministic():
     b = q.NF4Weight.quantize(w)
     for x, y in ((a.packed, b.packed), (a.code8, b.code8), (a.c2, b.c2), (a.mean, b.mean)):
         assert torch.equal(x, y)
+
+
+def test_codec_beyond_one_grid_pass():
+    """A weight larger than one pass of either codec grid (at most 16384
+    workgroups: 2^25 elements per pass of the quantizer's block kernel, 2^28
+    per pass of the dequantizer), ending in a ragged block: bit-exact end to
+    end, every element."""
+    n = (1 << 28) + 4099
+    _check(workloads.weight((1, n), 7100), "1 x (2^28 + 4099)")
