@@ -137,13 +137,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restric
 // ((v0+v1)+(v2+v3))+((v4+v5)+(v6+v7)), then level by level in LDS,
 // s'[t] = s[2t] + s[2t+1].  Because chunks are aligned powers of two,
 // applying this again to the partials reproduces the global tree exactly.
+// The last level (at most 2048 partials) runs at the start of pass 3.
 // ---------------------------------------------------------------------------
+// Tree sum of chunk `chunk`, called by every thread of the workgroup; the
+// result is in s[0] on return (after a barrier).
 template <typename Tin>
-__global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ in, int64_t len,
-                                                       double *__restrict__ out) {
-  __shared__ double s[kThreads];
+__device__ __forceinline__ void tree_chunk(const Tin *__restrict__ in, int64_t len, int64_t chunk, double *s) {
   const int t = threadIdx.x;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kTreeChunk + t * 8;
+  const int64_t base = chunk * kTreeChunk + t * 8;
   double v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (base + i < len) ? static_cast<double>(in[base + i]) : 0.0;
@@ -156,24 +157,34 @@ __global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ i
     if (t < width) s[t] = tmp;
     __syncthreads();
   }
-  if (t == 0) out[blockIdx.x] = s[0];
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ in, int64_t len,
+                                                       double *__restrict__ out) {
+  __shared__ double s[kThreads];
+  tree_chunk(in, len, blockIdx.x, s);
+  if (threadIdx.x == 0) out[blockIdx.x] = s[0];
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3.  mean = fl32(sum / nb).  One wave per group of 256 constants, 4 per
+// Pass 3.  Every workgroup first sums the last tree level (plen <= 2048
+// partials, the same tree as pass 2), then mean = fl32(sum / nb).  One wave
+// per group of 256 constants, 4 per
 // lane: d = fl32(c - mean), c2 = max |d| over the group, code = number of T8
 // thresholds below fl32(d / c2) (binary search over the 255 thresholds, with
 // +inf as a 256th sentinel).  c2 = 0 -> code 127.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restrict__ absmax, int64_t nb,
-                                                           const double *__restrict__ sum,
+                                                           const double *__restrict__ partials, int64_t plen,
                                                            uint8_t *__restrict__ code8,
                                                            float *__restrict__ c2,
                                                            float *__restrict__ mean_out) {
   __shared__ float thr[256];
+  __shared__ double s[kThreads];
   for (int i = threadIdx.x; i < 256; i += kThreads) thr[i] = (i < 255) ? u2f(cT8Thresh[i]) : INFINITY;
-  __syncthreads();
-  const float mean = static_cast<float>(sum[0] / static_cast<double>(nb));
+  tree_chunk(partials, plen, 0, s);                    // ends with a barrier: thr is ready too
+  const float mean = static_cast<float>(s[0] / static_cast<double>(nb));
   if (blockIdx.x == 0 && threadIdx.x == 0) mean_out[0] = mean;
 
   const int lane = threadIdx.x & 63;
@@ -320,7 +331,7 @@ hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uin
                      s, absmax, len, buf0);
   len = tree_partials(len);
   double *cur = buf0, *nxt = buf1;
-  while (len > 1) {
+  while (len > kTreeChunk) {
     hipLaunchKernelGGL(k_tree_sum<double>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads),
                        0, s, cur, len, nxt);
     len = tree_partials(len);
@@ -328,7 +339,7 @@ hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uin
   }
   const int64_t nb2 = (nb + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_quant_consts, dim3(grid_for(nb2, kThreads / 64, 4096)), dim3(kThreads), 0, s,
-                     absmax, nb, cur, code8, c2, mean);
+                     absmax, nb, cur, len, code8, c2, mean);
   return hipGetLastError();
 }
 
