@@ -5,8 +5,10 @@
 // Fine-Tune 70B on One GPU", The three innovations / 1-2):
 //   pass 1  k_quant_blocks   one read of W: per-64 absmax, NF4 codes, nibbles
 //   pass 2  k_tree_sum       fp64 pairwise tree of the absmax values (fixed
-//                            order, one or more levels of aligned 2048-chunks)
-//   pass 3  k_quant_consts   mean, per-256 scale c2, 8-bit constant codes
+//                            order, levels of aligned 2048-chunks until at
+//                            most 2048 partials remain)
+//   pass 3  k_quant_consts   last tree level, mean, per-256 scale c2, 8-bit
+//                            constant codes
 // Dequantize: k_dequant     packed codes -> bf16, one read, one write.
 //
 // Bit-exactness rules: fp32 division is IEEE correctly rounded (hipcc's
