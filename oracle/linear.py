@@ -42,6 +42,11 @@ def lora_down(X, A):
     return _f64(X) @ _f64(A).T
 
 
+def lora_grad_in(dY, B):
+    """G = dY B in fp64 (the adapter-side gradient before the scale)."""
+    return _f64(dY) @ _f64(B)
+
+
 def linear_fwd(X, Wt, A, B, scale):
     """Returns (Y, T) in fp64."""
     X, Wt, A, B = _f64(X), _f64(Wt), _f64(A), _f64(B)
@@ -56,7 +61,7 @@ def linear_bwd(dY, X, Wt, A, B, scale):
     dY, X, Wt, A, B = _f64(dY), _f64(X), _f64(Wt), _f64(A), _f64(B)
     s = float(np.float32(scale))
     T = X @ A.T
-    G = dY @ B
+    G = lora_grad_in(dY, B)
     dX = dY @ Wt + s * (G @ A)
     dA = s * (G.T @ X)
     dB = s * (dY.T @ T)

@@ -226,3 +226,35 @@ def test_golden_small_tensor():
     assert np.array_equal(q["c2"], g["c2"])
     assert q["mean"] == g["mean"][0]
     assert np.array_equal(nf4.dequantize_q(q), g["wt"])
+
+
+def test_decoded_constants_within_the_second_level_error_bound():
+    """Nearest-level coding bounds the decode error: with d = fl32(c - mean)
+    and k its 8-bit code, |d / c2 - T8[k]| is at most half the larger table gap
+    next to k, so |c_hat - c| <= c2 * that half gap plus the four fp32
+    roundings of d, d / c2, the product and the sum.  Checked for every block
+    with exact rational arithmetic, on groups whose scales differ by up to 7x
+    (a dropped mean, a sign slip or a group index taken modulo 256 breaks it
+    by orders of magnitude)."""
+    rng = np.random.default_rng(31)
+    groups = 12
+    sig = np.array([0.002, 0.05, 0.01, 0.12, 0.004, 0.03, 0.08, 0.002, 0.02, 0.06, 0.007, 0.1])
+    w = (rng.standard_normal((groups, 256 * 64)) * sig[:, None]).astype(np.float32).reshape(-1)
+    q = nf4.quantize(w)
+    chat = nf4.decode_constants(q["code8"], q["c2"], q["mean"])
+    t8 = nf4.t8_levels().astype(np.float64)
+    gaps = np.diff(t8)
+    half = np.zeros(256)
+    half[0] = gaps[0] / 2
+    half[255] = gaps[-1] / 2
+    half[1:255] = np.maximum(gaps[:-1], gaps[1:]) / 2
+    mean = float(q["mean"])
+    for b in range(len(q["absmax"])):
+        c = float(q["absmax"][b])
+        c2 = float(q["c2"][b // 256])
+        k = int(q["code8"][b])
+        ulp = float(np.spacing(np.float32(max(abs(c), abs(mean), c2))))
+        bound = Fraction(c2) * Fraction(half[k]) + 4 * Fraction(ulp)
+        assert abs(Fraction(float(chat[b])) - Fraction(c)) <= bound, b
+    # the scales really differ between groups
+    assert q["c2"].max() > 4 * q["c2"].min()

@@ -55,6 +55,14 @@ def test_row_subset_matches_the_full_mask():
     full = od.keep_mask(40, 96, 0.2, 77)
     rows = np.array([0, 7, 39])
     assert np.array_equal(od.keep_mask_rows(rows, 96, 0.2, 77), full[rows])
+    # rows that start inside a counter block (K % 4 != 0)
+    full = od.keep_mask(9, 70, 0.4, 79)
+    rows = np.array([1, 2, 5, 8])
+    assert np.array_equal(od.keep_mask_rows(rows, 70, 0.4, 79), full[rows])
+    # element by element against the word layout
+    seed = 79
+    words = od.philox4x32_10(np.array([[b, 0, 0, 0] for b in range(158)], np.uint32), (seed, 0)).reshape(-1)
+    assert np.array_equal(full.reshape(-1), words[:630] >= od.threshold(0.4))
 
 
 def test_bits_round_trip():
@@ -111,3 +119,29 @@ def test_backward_matches_finite_differences_for_a_fixed_mask():
     m, k = np.argwhere(~keep)[0]
     base_only = (olin._f64(dY) @ olin._f64(Wt))[m, k]
     assert abs(dX[m, k] - base_only) <= 1e-12
+
+
+@pytest.mark.parametrize("p", [0.05, 0.3])
+def test_inverted_dropout_keeps_the_branch_unbiased(p):
+    """Inverted dropout is defined so that the scaled, dropped input has the
+    expected value of the undropped one: E[s_eff X_d] = s X.  Measured through
+    the oracle layer itself: X = 1, A = 1 (r = 1) and W = 0 give T[m] =
+    s_eff * (number of kept elements of row m); over 2^22 Philox draws the
+    mean of T / K must be s within 5 standard errors of the keep rate.  A
+    scale of s (1 - p), s (1 + p), s / (1 + p) or plain s misses it by 0.25 %
+    or more, far beyond the bound (about 0.06 % at p = 0.05)."""
+    M, K, s = 1024, 4096, 0.25
+    one = round_fp32_to_bf16_bits(np.ones((M, K), np.float32))
+    A = round_fp32_to_bf16_bits(np.ones((1, K), np.float32))
+    B = round_fp32_to_bf16_bits(np.zeros((8, 1), np.float32))
+    Wt = np.zeros((8, K))
+    keep = od.keep_mask(M, K, p, seed=4321)
+    _, T = od.linear_fwd(one, Wt, A, B, s, p, keep)
+    ratio = float(np.mean(T)) / K / s
+    sigma = np.sqrt(p * (1 - p) / (M * K)) / (1 - p)
+    assert abs(ratio - 1.0) <= 5 * sigma + 1e-6, (ratio, sigma)
+    # the factor is the fp32 rounding of the exact quotient (within half an ulp)
+    from fractions import Fraction
+    se = od.effective_scale(s, p)
+    exact = Fraction(float(np.float32(s))) / (1 - Fraction(float(p)))
+    assert abs(Fraction(float(se)) - exact) <= Fraction(float(np.spacing(se))) / 2
