@@ -256,6 +256,7 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
   const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grads_workspace_bytes(M, N, K, r))
     return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;   // nothing to reduce: dA and dB are left as they were
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int m = static_cast<int>(M);
   if (dA) {

@@ -40,6 +40,26 @@ def _need(t, dtype, name, shape=None):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
+def _workspace(workspace, need, device):
+    """(tensor or None, bytes passed to the C ABI): the caller's workspace, or
+    a fresh one of `need` bytes.  The byte count handed to the library is the
+    buffer's real size, so the C-side QLORA_ERR_WORKSPACE check guards it."""
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a tensor")
+    have = workspace.numel() * workspace.element_size()
+    if have < need:
+        raise ValueError("workspace holds %d bytes, %d needed" % (have, need))
+    if workspace.device.type != "cuda":
+        raise ValueError("workspace must be on a GPU device")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace, have
+
+
 def nf4_sizes(n):
     pb, nb, nb2 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     check(lib().qlora_nf4_sizes(int(n), ctypes.byref(pb), ctypes.byref(nb), ctypes.byref(nb2)), "qlora_nf4_sizes")
@@ -123,11 +143,30 @@ class NF4Weight:
         return sum(t.numel() * t.element_size() for t in (self.packed, self.code8, self.c2, self.mean))
 
 
-def _lin_checks(X, w, A, B, r_expect=None):
+def _mat(t, name, dtype=torch.bfloat16):
+    """A 2-D contiguous device tensor of `dtype`; returns its shape."""
+    _need(t, dtype, name)
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    return tuple(t.shape)
+
+
+def _out(t, shape, device, name, dtype=torch.bfloat16):
+    """The caller's output tensor (checked) or a fresh one."""
+    if t is None:
+        return torch.empty(*shape, dtype=dtype, device=device)
+    _need(t, dtype, name, shape)
+    return t
+
+
+def _lin_checks(X, w, A, B):
     N, K = w.rows, w.cols
+    _need(X, torch.bfloat16, "X")
     if X.dim() != 2 or X.shape[1] != K:
         raise ValueError("X must be [M, %d]" % K)
-    _need(X, torch.bfloat16, "X")
+    _need(A, torch.bfloat16, "A")
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D [r, K]")
     r = A.shape[0]
     _need(A, torch.bfloat16, "A", (r, K))
     _need(B, torch.bfloat16, "B", (N, r))
@@ -137,29 +176,23 @@ def _lin_checks(X, w, A, B, r_expect=None):
 def linear_fwd(X, w, A, B, scale, T_out=None, out=None, workspace=None):
     """Y = X deq(W)^T + scale (X A^T) B^T; returns (Y, T) with T = scale X A^T [M, r]."""
     M, N, K, r = _lin_checks(X, w, A, B)
-    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
-    _need(Y, torch.bfloat16, "Y", (M, N))
-    T = T_out if T_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
-    _need(T, torch.bfloat16, "T", (M, r))
-    ws_bytes = lib().qlora_linear_workspace_bytes(M, N, K, r, 0)
-    ws = None
-    if ws_bytes:
-        ws = workspace if workspace is not None else torch.empty(ws_bytes, dtype=torch.uint8, device=X.device)
-        if ws.numel() * ws.element_size() < ws_bytes:
-            raise ValueError("workspace smaller than %d bytes" % ws_bytes)
+    Y = _out(out, (M, N), X.device, "Y")
+    T = _out(T_out, (M, r), X.device, "T")
+    ws, ws_bytes = _workspace(workspace, lib().qlora_linear_workspace_bytes(M, N, K, r, 0), X.device)
     st = w.struct()
     check(lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(Y),
-                                 _ptr(T), None if ws is None else _ptr(ws), ws_bytes, _stream(X)),
-          "qlora_linear_fwd")
+                                 _ptr(T), _ptr(ws), ws_bytes, _stream(X)), "qlora_linear_fwd")
     return Y, T
 
 
-def linear_fwd_group(linears, scale=None, workspace=None):
+def linear_fwd_group(linears, workspace=None):
     """Forward of up to 8 independent linears sharing the token count M.
 
     `linears` is a sequence of (X, w, A, B, scale) or (X, w, A, B, scale, T_out,
     Y_out) tuples; returns the list of (Y, T).  Same results as calling
-    linear_fwd on each; in the decode regime the group costs two launches."""
+    linear_fwd on each (bit for bit except on the streaming decode route,
+    within the tolerance there); in the decode regime the group costs the
+    launches of one call."""
     from ._capi import LinearDescStruct
     if not 1 <= len(linears) <= 8:
         raise ValueError("a group holds 1 to 8 linears")
@@ -174,29 +207,23 @@ def linear_fwd_group(linears, scale=None, workspace=None):
             M = m
         elif m != M:
             raise ValueError("all linears of a group share M")
-        Y = Y_out if Y_out is not None else torch.empty(m, N, dtype=torch.bfloat16, device=X.device)
-        _need(Y, torch.bfloat16, "Y", (m, N))
-        T = T_out if T_out is not None else torch.empty(m, r, dtype=torch.bfloat16, device=X.device)
-        _need(T, torch.bfloat16, "T", (m, r))
+        Y = _out(Y_out, (m, N), X.device, "Y")
+        T = _out(T_out, (m, r), X.device, "T")
         st = w.struct()
         structs.append(st)
         descs.append(LinearDescStruct(X.data_ptr(), ctypes.pointer(st), A.data_ptr(), B.data_ptr(), r, float(sc),
                                       Y.data_ptr(), T.data_ptr()))
         outs.append((Y, T))
     arr = (LinearDescStruct * len(descs))(*descs)
-    ws_bytes = lib().qlora_linear_group_workspace_bytes(len(descs), arr, M)
-    ws = None
-    if ws_bytes:
-        ws = workspace if workspace is not None else torch.empty(ws_bytes, dtype=torch.uint8,
-                                                                  device=linears[0][0].device)
-        if ws.numel() * ws.element_size() < ws_bytes:
-            raise ValueError("workspace smaller than %d bytes" % ws_bytes)
-    check(lib().qlora_linear_fwd_group(len(descs), arr, M, None if ws is None else _ptr(ws), ws_bytes,
-                                       _stream(linears[0][0])), "qlora_linear_fwd_group")
+    dev = linears[0][0].device
+    ws, ws_bytes = _workspace(workspace, lib().qlora_linear_group_workspace_bytes(len(descs), arr, M), dev)
+    check(lib().qlora_linear_fwd_group(len(descs), arr, M, _ptr(ws), ws_bytes, _stream(linears[0][0])),
+          "qlora_linear_fwd_group")
     return outs
 
 
-def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=True, workspace=None):
+def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=True, workspace=None,
+               dX_out=None, dA_out=None, dB_out=None):
     """Returns (dX, dA, dB) (None where not requested); T = scale X A^T as
     returned by linear_fwd, or None (recomputed)."""
     M, N, K, r = _lin_checks(X, w, A, B)
@@ -204,11 +231,10 @@ def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=Tru
     if T is not None:
         _need(T, torch.bfloat16, "T", (M, r))
     dev = X.device
-    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev) if need_dX else None
-    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev) if need_dA else None
-    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
-    ws_bytes = lib().qlora_linear_workspace_bytes(M, N, K, r, 1)
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    dX = _out(dX_out, (M, K), dev, "dX") if need_dX else None
+    dA = _out(dA_out, (r, K), dev, "dA") if need_dA else None
+    dB = _out(dB_out, (N, r), dev, "dB") if need_dB else None
+    ws, ws_bytes = _workspace(workspace, lib().qlora_linear_workspace_bytes(M, N, K, r, 1), dev)
     st = w.struct()
     check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(T), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
                                  float(scale), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(X)),
@@ -220,11 +246,10 @@ def linear_bwd(dY, X, T, w, A, B, scale, need_dX=True, need_dA=True, need_dB=Tru
 
 def lora_down(X, A, scale, out=None):
     """T = scale X A^T."""
-    M, K = X.shape
-    r = A.shape[0]
-    _need(X, torch.bfloat16, "X")
+    M, K = _mat(X, "X")
+    r = _mat(A, "A")[0]
     _need(A, torch.bfloat16, "A", (r, K))
-    T = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    T = _out(out, (M, r), X.device, "T")
     check(lib().qlora_lora_down(_ptr(X), M, K, _ptr(A), r, float(scale), _ptr(T), _stream(X)), "qlora_lora_down")
     return T
 
@@ -238,16 +263,16 @@ def _arrays(ptrs, rs, scales=None):
 def lora_down_shared(X, As, scales, outs=None):
     """[T_i = scale_i X A_i^T] for linears that share X (qlora_lora_down_shared):
     one launch, bit-identical to lora_down per linear."""
-    M, K = X.shape
-    _need(X, torch.bfloat16, "X")
+    M, K = _mat(X, "X")
     if not 1 <= len(As) <= 8 or len(scales) != len(As):
         raise ValueError("1 to 8 members, one scale each")
+    if outs is not None and len(outs) != len(As):
+        raise ValueError("one output per member")
     Ts = []
     for i, A in enumerate(As):
-        _need(A, torch.bfloat16, "A", (A.shape[0], K))
-        T = outs[i] if outs is not None else torch.empty(M, A.shape[0], dtype=torch.bfloat16, device=X.device)
-        _need(T, torch.bfloat16, "T", (M, A.shape[0]))
-        Ts.append(T)
+        r = _mat(A, "A")[0]
+        _need(A, torch.bfloat16, "A", (r, K))
+        Ts.append(_out(None if outs is None else outs[i], (M, r), X.device, "T"))
     pa, ra, sa = _arrays([A.data_ptr() for A in As], [A.shape[0] for A in As], scales)
     pt, _, _ = _arrays([T.data_ptr() for T in Ts], [1] * len(Ts))
     check(lib().qlora_lora_down_shared(_ptr(X), M, K, len(As), pa, ra, sa, pt, _stream(X)), "qlora_lora_down_shared")
@@ -258,78 +283,66 @@ def lora_dA_shared(X, Gs, outs=None, workspace=None):
     """[dA_i = G_i^T X] for linears that share X (qlora_lora_dA_shared; G_i
     carries the scale): one launch (+ the split sums), bit-identical to the dA
     of lora_grads per linear."""
-    M, K = X.shape
-    _need(X, torch.bfloat16, "X")
+    M, K = _mat(X, "X")
     if not 1 <= len(Gs) <= 8:
         raise ValueError("1 to 8 members")
+    if outs is not None and len(outs) != len(Gs):
+        raise ValueError("one output per member")
     dAs = []
     for i, G in enumerate(Gs):
-        _need(G, torch.bfloat16, "G", (M, G.shape[1]))
-        dA = outs[i] if outs is not None else torch.empty(G.shape[1], K, dtype=torch.bfloat16, device=X.device)
-        _need(dA, torch.bfloat16, "dA", (G.shape[1], K))
-        dAs.append(dA)
+        r = _mat(G, "G")[1]
+        _need(G, torch.bfloat16, "G", (M, r))
+        dAs.append(_out(None if outs is None else outs[i], (r, K), X.device, "dA"))
     pg, ra, _ = _arrays([G.data_ptr() for G in Gs], [G.shape[1] for G in Gs])
     pd, _, _ = _arrays([dA.data_ptr() for dA in dAs], [1] * len(dAs))
-    ws_bytes = lib().qlora_lora_dA_shared_workspace_bytes(M, K, len(Gs), ra)
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=X.device)
-    if ws.numel() * ws.element_size() < ws_bytes:
-        raise ValueError("workspace smaller than %d bytes" % ws_bytes)
+    ws, ws_bytes = _workspace(workspace, lib().qlora_lora_dA_shared_workspace_bytes(M, K, len(Gs), ra), X.device)
     check(lib().qlora_lora_dA_shared(_ptr(X), M, K, len(Gs), pg, ra, pd, _ptr(ws), ws_bytes, _stream(X)),
           "qlora_lora_dA_shared")
     return dAs
 
 
-def dropout_mask(X, p, seed):
+def dropout_mask(X, p, seed, out=None, keep_out=None):
     """(X_d, keep): the LoRA input with dropout p (qlora_dropout_mask); keep is
     int32 [M, K / 32], bit k % 32 of word k / 32."""
-    M, K = X.shape
-    _need(X, torch.bfloat16, "X")
-    Xd = torch.empty_like(X)
-    keep = torch.empty(M, K // 32, dtype=torch.int32, device=X.device)
+    M, K = _mat(X, "X")
+    Xd = _out(out, (M, K), X.device, "X_d")
+    keep = _out(keep_out, (M, K // 32), X.device, "keep", torch.int32)
     check(lib().qlora_dropout_mask(_ptr(X), M, K, float(p), int(seed), _ptr(Xd), _ptr(keep), _stream(X)),
           "qlora_dropout_mask")
     return Xd, keep
 
 
-def dropout_apply(X, keep):
+def dropout_apply(X, keep, out=None):
     """X_d from X and a keep mask (qlora_dropout_apply)."""
-    M, K = X.shape
-    _need(X, torch.bfloat16, "X")
+    M, K = _mat(X, "X")
     _need(keep, torch.int32, "keep", (M, K // 32))
-    Xd = torch.empty_like(X)
+    Xd = _out(out, (M, K), X.device, "X_d")
     check(lib().qlora_dropout_apply(_ptr(X), M, K, _ptr(keep), _ptr(Xd), _stream(X)), "qlora_dropout_apply")
     return Xd
 
 
 def nf4_matmul_dx_dropout(dY, w, G, A, keep, out=None):
     """dX = dY deq(W) + (G A) * keep (G = s_eff dY B)."""
-    M = dY.shape[0]
-    r = A.shape[0]
+    M = _mat(dY, "dY")[0]
+    r = _mat(A, "A")[0]
     _need(dY, torch.bfloat16, "dY", (M, w.rows))
     _need(G, torch.bfloat16, "G", (M, r))
     _need(A, torch.bfloat16, "A", (r, w.cols))
     _need(keep, torch.int32, "keep", (M, w.cols // 32))
-    dX = out if out is not None else torch.empty(M, w.cols, dtype=torch.bfloat16, device=dY.device)
+    dX = _out(out, (M, w.cols), dY.device, "dX")
     st = w.struct()
     check(lib().qlora_nf4_matmul_dx_dropout(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, _ptr(keep), _ptr(dX),
                                             _stream(dY)), "qlora_nf4_matmul_dx_dropout")
     return dX
 
 
-def dropout_scale(scale, p):
-    """s_eff = fl32(s / (1 - p)), the LoRA scale with inverted dropout."""
-    import numpy as np
-    return float(np.float32(float(np.float32(scale)) / (1.0 - float(np.float32(p)))))
-
-
-def linear_fwd_dropout(X, w, A, B, scale, p, seed, T_out=None, out=None, workspace=None):
+def linear_fwd_dropout(X, w, A, B, scale, p, seed, T_out=None, out=None, keep_out=None, workspace=None):
     """Forward with LoRA dropout: returns (Y, T, keep)."""
     M, N, K, r = _lin_checks(X, w, A, B)
-    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
-    T = T_out if T_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
-    keep = torch.empty(M, K // 32, dtype=torch.int32, device=X.device)
-    ws_bytes = lib().qlora_linear_dropout_workspace_bytes(M, N, K, r, 0)
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=X.device)
+    Y = _out(out, (M, N), X.device, "Y")
+    T = _out(T_out, (M, r), X.device, "T")
+    keep = _out(keep_out, (M, K // 32), X.device, "keep", torch.int32)
+    ws, ws_bytes = _workspace(workspace, lib().qlora_linear_dropout_workspace_bytes(M, N, K, r, 0), X.device)
     st = w.struct()
     check(lib().qlora_linear_fwd_dropout(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), float(p),
                                          int(seed), _ptr(Y), _ptr(T), _ptr(keep), _ptr(ws), ws_bytes, _stream(X)),
@@ -338,17 +351,19 @@ def linear_fwd_dropout(X, w, A, B, scale, p, seed, T_out=None, out=None, workspa
 
 
 def linear_bwd_dropout(dY, X, T, w, A, B, scale, p, keep, need_dX=True, need_dA=True, need_dB=True,
-                       workspace=None):
-    """Backward with LoRA dropout given the forward's keep mask: (dX, dA, dB)."""
+                       workspace=None, dX_out=None, dA_out=None, dB_out=None):
+    """Backward with LoRA dropout given the forward's keep mask: (dX, dA, dB);
+    T as returned by linear_fwd_dropout, or None (recomputed)."""
     M, N, K, r = _lin_checks(X, w, A, B)
     _need(dY, torch.bfloat16, "dY", (M, N))
     _need(keep, torch.int32, "keep", (M, K // 32))
+    if T is not None:
+        _need(T, torch.bfloat16, "T", (M, r))
     dev = X.device
-    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev) if need_dX else None
-    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev) if need_dA else None
-    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
-    ws_bytes = lib().qlora_linear_dropout_workspace_bytes(M, N, K, r, 1)
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    dX = _out(dX_out, (M, K), dev, "dX") if need_dX else None
+    dA = _out(dA_out, (r, K), dev, "dA") if need_dA else None
+    dB = _out(dB_out, (N, r), dev, "dB") if need_dB else None
+    ws, ws_bytes = _workspace(workspace, lib().qlora_linear_dropout_workspace_bytes(M, N, K, r, 1), dev)
     st = w.struct()
     check(lib().qlora_linear_bwd_dropout(_ptr(dY), _ptr(X), _ptr(T), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
                                          float(scale), float(p), _ptr(keep), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
@@ -358,12 +373,12 @@ def linear_bwd_dropout(dY, X, T, w, A, B, scale, p, keep, need_dX=True, need_dA=
 
 def nf4_matmul_fwd(X, w, T, B, out=None):
     """Y = X deq(W)^T + T B^T (T = scale X A^T)."""
-    M = X.shape[0]
-    r = B.shape[1]
+    M = _mat(X, "X")[0]
+    r = _mat(B, "B")[1]
     _need(X, torch.bfloat16, "X", (M, w.cols))
     _need(T, torch.bfloat16, "T", (M, r))
     _need(B, torch.bfloat16, "B", (w.rows, r))
-    Y = out if out is not None else torch.empty(M, w.rows, dtype=torch.bfloat16, device=X.device)
+    Y = _out(out, (M, w.rows), X.device, "Y")
     st = w.struct()
     check(lib().qlora_nf4_matmul_fwd(_ptr(X), M, ctypes.byref(st), _ptr(T), _ptr(B), r, _ptr(Y), _stream(X)),
           "qlora_nf4_matmul_fwd")
@@ -372,15 +387,11 @@ def nf4_matmul_fwd(X, w, T, B, out=None):
 
 def lora_grad_in(dY, B, scale, out=None, workspace=None):
     """G = scale dY B."""
-    M, N = dY.shape
-    r = B.shape[1]
-    _need(dY, torch.bfloat16, "dY")
+    M, N = _mat(dY, "dY")
+    r = _mat(B, "B")[1]
     _need(B, torch.bfloat16, "B", (N, r))
-    G = out if out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=dY.device)
-    ws_bytes = lib().qlora_lora_grad_in_workspace_bytes(N, r)
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dY.device)
-    if ws.numel() * ws.element_size() < ws_bytes:
-        raise ValueError("workspace smaller than %d bytes" % ws_bytes)
+    G = _out(out, (M, r), dY.device, "G")
+    ws, ws_bytes = _workspace(workspace, lib().qlora_lora_grad_in_workspace_bytes(N, r), dY.device)
     check(lib().qlora_lora_grad_in(_ptr(dY), M, N, _ptr(B), r, float(scale), _ptr(G), _ptr(ws), ws_bytes,
                                    _stream(dY)), "qlora_lora_grad_in")
     return G
@@ -388,28 +399,30 @@ def lora_grad_in(dY, B, scale, out=None, workspace=None):
 
 def nf4_matmul_dx(dY, w, G, A, out=None):
     """dX = dY deq(W) + G A (G = scale dY B)."""
-    M = dY.shape[0]
-    r = A.shape[0]
+    M = _mat(dY, "dY")[0]
+    r = _mat(A, "A")[0]
     _need(dY, torch.bfloat16, "dY", (M, w.rows))
     _need(G, torch.bfloat16, "G", (M, r))
     _need(A, torch.bfloat16, "A", (r, w.cols))
-    dX = out if out is not None else torch.empty(M, w.cols, dtype=torch.bfloat16, device=dY.device)
+    dX = _out(out, (M, w.cols), dY.device, "dX")
     st = w.struct()
     check(lib().qlora_nf4_matmul_dx(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, _ptr(dX), _stream(dY)),
           "qlora_nf4_matmul_dx")
     return dX
 
 
-def lora_grads(X, dY, G, T, need_dA=True, need_dB=True, workspace=None):
+def lora_grads(X, dY, G, T, need_dA=True, need_dB=True, workspace=None, dA_out=None, dB_out=None):
     """dA = G^T X, dB = dY^T T (G and T carry the scale)."""
-    M, K = X.shape
-    N = dY.shape[1]
-    r = G.shape[1]
+    M, K = _mat(X, "X")
+    N = _mat(dY, "dY")[1]
+    r = _mat(G, "G")[1]
+    _need(dY, torch.bfloat16, "dY", (M, N))
+    _need(G, torch.bfloat16, "G", (M, r))
+    _need(T, torch.bfloat16, "T", (M, r))
     dev = X.device
-    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev) if need_dA else None
-    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev) if need_dB else None
-    ws_bytes = lib().qlora_lora_grads_workspace_bytes(M, N, K, r)
-    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    dA = _out(dA_out, (r, K), dev, "dA") if need_dA else None
+    dB = _out(dB_out, (N, r), dev, "dB") if need_dB else None
+    ws, ws_bytes = _workspace(workspace, lib().qlora_lora_grads_workspace_bytes(M, N, K, r), dev)
     check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(G), _ptr(T), M, N, K, r, _ptr(dA), _ptr(dB), _ptr(ws),
                                  ws_bytes, _stream(X)), "qlora_lora_grads")
     return dA, dB

@@ -11,11 +11,15 @@
  * GPU", The three innovations / 2).  Each pass dequantizes W to bf16 on the
  * fly inside the matmul and adds a 16-bit LoRA branch:
  *
- *     T  = X A^T                    Y  = X deq(W)^T + s T B^T
- *     G  = dY B                     dX = dY deq(W) + s G A
- *     dA = s G^T X                  dB = s dY^T T
+ *     T  = s X A^T                  Y  = X deq(W)^T + T B^T
+ *     G  = s dY B                   dX = dY deq(W) + G A
+ *     dA = G^T X                    dB = dY^T T
  *
- * with s = alpha / r.  No gradient is formed for W, which is frozen.
+ * with s = alpha / r.  This is the pages' layer Y = X W^T + s X A^T B^T
+ * with the scale folded into the rank-r intermediates: T and G carry s,
+ * applied once in fp32 before their single rounding to bf16, so the fused
+ * matmuls add T B^T and G A as plain contraction steps.  No gradient is
+ * formed for W, which is frozen.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -29,6 +33,13 @@
  *    anything is launched: on any error nothing is launched or written.  A
  *    failed launch returns QLORA_ERR_HIP.
  *  - Gradients overwrite their outputs (no accumulation).
+ *  - M = 0 (no tokens) is valid everywhere a token count is taken: the call
+ *    validates its arguments, launches nothing and writes nothing (dA and dB,
+ *    which would be zero, are left as they were).
+ *  - The linear-layer calls take W [N, K] with K % 64 == 0 (a 64-block never
+ *    straddles a row), N % 8 == 0 (16-byte rows of Y and dB) and every size
+ *    below 2^31 (M * max(N, K) included); the codec calls take any
+ *    rows, cols >= 1 with rows * cols < 2^31.
  *  - Results are deterministic: no floating-point atomics are used, so two
  *    calls on the same inputs give the same bits.
  *  - Inputs with NaN or Inf are outside the contract (outputs unspecified).
@@ -46,7 +57,7 @@ extern "C" {
 typedef enum {
   QLORA_OK = 0,
   QLORA_ERR_INVALID_ARG = -1,       /* null/misaligned pointer, negative size, bad scale */
-  QLORA_ERR_UNSUPPORTED_SHAPE = -2, /* K % 64 != 0, r outside [1, 128], size overflow */
+  QLORA_ERR_UNSUPPORTED_SHAPE = -2, /* K % 64 != 0, N % 8 != 0, r outside [1, 128], size >= 2^31 */
   QLORA_ERR_WORKSPACE = -3,         /* workspace missing or smaller than required */
   QLORA_ERR_HIP = -4                /* a HIP runtime call or kernel launch failed */
 } qlora_status;
@@ -109,7 +120,9 @@ size_t qlora_quantize_workspace_bytes(int64_t n);
  * the 8-bit table, ties low (group scale 0 -> code 127).  Bit-exact and
  * deterministic.  Pages: automatone.win, "QLoRA paper explained", How it
  * works / 4-bit NormalFloat and Double Quantization.
- * Requires rows, cols >= 1 and ws_bytes >= qlora_quantize_workspace_bytes. */
+ * Requires rows, cols >= 1, rows * cols < 2^31 (UNSUPPORTED_SHAPE otherwise;
+ * the largest LLaMA-65B weight has 1.8e8 elements) and ws_bytes >=
+ * qlora_quantize_workspace_bytes. */
 int qlora_quantize_nf4(const float *W, const qlora_nf4_weight *out, void *ws,
                        size_t ws_bytes, void *stream);
 
@@ -143,8 +156,9 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
 /* Forward: Y [M, N] = X [M, K] deq(W)^T + scale (X A^T) B^T.
  *   X [M, K], A [r, K], B [N, r], Y [M, N]: bf16.  W: N x K NF4 weight.
  *   T_out [M, r] (nullable): receives T = scale X A^T in bf16 (the LoRA
- *   intermediate with the scale applied once in fp32 before rounding) for
- *   reuse in the backward pass; when NULL, T lives in the workspace.
+ *   intermediate with the scale applied once in fp32 before rounding, not
+ *   the unscaled X A^T) for reuse in the backward pass; when NULL, T lives
+ *   in the workspace.
  *   ws: device memory of qlora_linear_workspace_bytes(M, N, K, r, 0) bytes,
  *   16-byte aligned; it may be NULL only when that size is 0.
  *   At 1 <= M <= 64 with r % 8 == 0 the pass takes a decode-regime route that
@@ -156,8 +170,9 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
  *   instead of rounding NF4[q] * c_hat to bf16 (within the same tolerance).
  *   Otherwise two MFMA tile kernels that dequantize exactly as
  *   qlora_dequantize_nf4 does.
- * Requires K % 64 == 0 (blocks never straddle rows), 1 <= r <= 128, M >= 0
- * (M = 0 launches nothing), N >= 1.  Pages: automatone.win, "QLoRA paper
+ * Requires K % 64 == 0 (blocks never straddle rows), N % 8 == 0, 1 <= r <=
+ * 128, M >= 0 (M = 0 launches nothing), M * max(N, K) < 2^31 (else
+ * UNSUPPORTED_SHAPE).  Pages: automatone.win, "QLoRA paper
  * explained", How it works; creativeworksofknowledge.com, "QLoRA: Fine-Tune
  * 70B on One GPU", Code (r, lora_alpha, bias="none"). */
 int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
@@ -226,8 +241,10 @@ int qlora_linear_fwd_group(int count, const qlora_linear_desc *descs, int64_t M,
  *   dX [M, K] = dY deq(W) + scale (dY B) A        (nullable: skipped)
  *   dA [r, K] = scale (dY B)^T X                  (nullable: skipped)
  *   dB [N, r] = scale dY^T T                      (nullable: skipped)
- * all bf16.  No gradient for W (frozen).  Same shape rules as the forward.
- * dA and dB are reduced over M in a fixed order (deterministic).
+ * all bf16.  No gradient for W (frozen).  Same shape rules as the forward
+ * (K % 64 == 0, N % 8 == 0, 1 <= r <= 128); M = 0 writes nothing.  T, when
+ * given, must be the scaled T of the forward pass.  dA and dB are reduced
+ * over M in a fixed order (deterministic).
  * Pages: automatone.win, "QLoRA paper explained", How it works (gradients
  * flow through the 4-bit base into the adapters only); gptget.net, "QLoRA:
  * Efficient Finetuning of Quantized LLMs", Deep Analysis / Methodology. */
@@ -275,7 +292,8 @@ size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t
  * contraction runs over M: when the d-tiles alone do not fill the GPU, M is
  * split and the fp32 split partials (in the workspace) are summed in split
  * order by a second pass (deterministic).  G and X are needed for dA (K % 8
- * == 0), dY and T for dB (N % 8 == 0). */
+ * == 0), dY and T for dB (N % 8 == 0).  M = 0 launches nothing and leaves dA
+ * and dB as they were. */
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
                      const uint16_t *T, int64_t M, int64_t N, int64_t K, int32_t r,
                      uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream);

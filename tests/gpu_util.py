@@ -47,3 +47,42 @@ def assert_close(got, ref, name=""):
     rel, emax = errors(got, ref)
     assert rel <= REL_FRO and emax <= REL_MAX, "%s: rel_fro=%.3g max=%.3g" % (name, rel, emax)
     return rel, emax
+
+
+GUARD = 4096   # bytes of guard band on each side of a guarded buffer
+
+
+class Guarded:
+    """A device buffer of `nbytes` payload bytes between two guard bands of
+    GUARD seeded pattern bytes.  The payload starts as 0xFF bytes (bf16 and
+    fp32 NaN), so an output element a kernel fails to write shows up as NaN,
+    and intact() reports whether a call wrote outside the payload."""
+
+    def __init__(self, nbytes, seed=0, fill=0xFF):
+        nbytes = int(nbytes)
+        self.nbytes = nbytes
+        g = np.random.default_rng(1000003 + seed)
+        self.pattern = torch.from_numpy(g.integers(0, 256, 2 * GUARD, dtype=np.uint8))
+        self.full = torch.empty(nbytes + 2 * GUARD, dtype=torch.uint8, device=DEV)
+        self.full[:GUARD].copy_(self.pattern[:GUARD])
+        self.full[GUARD + nbytes:].copy_(self.pattern[GUARD:])
+        self.payload = self.full[GUARD:GUARD + nbytes]
+        self.payload.fill_(fill)
+
+    def tensor(self, shape, dtype=torch.bfloat16):
+        return self.payload.view(dtype).view(*shape)
+
+    def intact(self):
+        torch.cuda.synchronize()
+        full = self.full.cpu()
+        return (torch.equal(full[:GUARD], self.pattern[:GUARD]) and
+                torch.equal(full[GUARD + self.nbytes:], self.pattern[GUARD:]))
+
+
+def guarded_like(shape, dtype=torch.bfloat16, seed=0):
+    """(Guarded, tensor of `shape`) for an output of that shape and dtype."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    g = Guarded(n * torch.empty((), dtype=dtype).element_size(), seed)
+    return g, g.tensor(shape, dtype)

@@ -185,3 +185,31 @@ def test_python_binding_rejects_cpu_tensors():
     W = torch.zeros(64, 64)
     with pytest.raises(ValueError):
         q.NF4Weight.quantize(W)
+
+
+def test_binding_workspace_checks_size_before_anything_else():
+    import torch
+    from bit_nf4_quantized_absmax_amd import ops
+    with pytest.raises(ValueError, match="100 needed"):
+        ops._workspace(torch.empty(99, dtype=torch.uint8), 100, None)
+    with pytest.raises(ValueError, match="needed"):
+        ops._workspace(torch.empty(24, dtype=torch.float32), 100, None)   # 96 bytes
+    with pytest.raises(ValueError, match="GPU"):
+        ops._workspace(torch.empty(100, dtype=torch.uint8), 100, None)
+    assert ops._workspace(None, 0, None) == (None, 0)
+
+
+def test_binding_has_no_method_arithmetic_exports():
+    # the LoRA dropout scale is computed by the library from (scale, p)
+    assert not hasattr(q, "dropout_scale")
+
+
+def test_zero_tokens_validate_and_return_ok():
+    L = q.lib()
+    P = ctypes.c_void_p(0x20000)
+    assert L.qlora_lora_grads(P, P, P, P, 0, 64, 64, 8, P, P, P, 1 << 20, None) == OK
+    assert L.qlora_lora_grads(P, P, P, P, 0, 64, 64, 8, P, P, None, 0, None) == WS     # still validated
+    assert L.qlora_lora_grad_in(P, 0, 64, P, 8, 1.0, P, P, 1 << 20, None) == OK
+    w = _fake_weight(64, 64)
+    assert L.qlora_linear_fwd_dropout(P, 0, ctypes.byref(w), P, P, 8, 1.0, 0.1, 1, P, None, P, P, 1 << 20,
+                                      None) == OK
