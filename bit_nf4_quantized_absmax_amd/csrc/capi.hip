@@ -44,6 +44,8 @@ int check_linear_shape(int64_t M, const qlora_nf4_weight *w, int32_t r, float sc
 
 bool bf16_ok(const void *p) { return p && aligned(p, 16); }
 bool bf16_opt(const void *p) { return !p || aligned(p, 16); }
+// A tensor with M rows: at M = 0 it has no storage and its pointer may be NULL.
+bool rows_ok(const void *p, int64_t M) { return M == 0 ? bf16_opt(p) : bf16_ok(p); }
 
 NF4View view_of(const qlora_nf4_weight *w) {
   return NF4View{w->packed, w->code8, w->c2, w->mean, static_cast<int>(w->rows), static_cast<int>(w->cols),
@@ -154,7 +156,7 @@ int qlora_lora_down(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A, 
   if (M < 0 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
   if (K < 8 || K % 8 || r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > kMaxElems / K) return QLORA_ERR_UNSUPPORTED_SHAPE;
-  if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(T)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(X, M) || !bf16_ok(A) || !rows_ok(T, M)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_lora_down(X, static_cast<int>(M), static_cast<int>(K), A, r, scale, T,
                                    static_cast<hipStream_t>(stream)));
@@ -173,9 +175,9 @@ int qlora_lora_down_shared(const uint16_t *X, int64_t M, int64_t K, int count, c
                            const int32_t *r, const float *scale, uint16_t *const *T, void *stream) {
   int st = check_shared(M, K, count, r);
   if (st) return st;
-  if (!A || !scale || !T || !bf16_ok(X)) return QLORA_ERR_INVALID_ARG;
+  if (!A || !scale || !T || !rows_ok(X, M)) return QLORA_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i)
-    if (!bf16_ok(A[i]) || !bf16_ok(T[i]) || !isfinite(scale[i])) return QLORA_ERR_INVALID_ARG;
+    if (!bf16_ok(A[i]) || !rows_ok(T[i], M) || !isfinite(scale[i])) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_lora_down_shared(X, static_cast<int>(M), static_cast<int>(K), count, A, r, scale, T,
                                           static_cast<hipStream_t>(stream)));
@@ -190,9 +192,9 @@ int qlora_lora_dA_shared(const uint16_t *X, int64_t M, int64_t K, int count, con
                          const int32_t *r, uint16_t *const *dA, void *ws, size_t ws_bytes, void *stream) {
   int st = check_shared(M, K, count, r);
   if (st) return st;
-  if (!G || !dA || !bf16_ok(X)) return QLORA_ERR_INVALID_ARG;
+  if (!G || !dA || !rows_ok(X, M)) return QLORA_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i)
-    if (!bf16_ok(G[i]) || !bf16_ok(dA[i])) return QLORA_ERR_INVALID_ARG;
+    if (!rows_ok(G[i], M) || !bf16_ok(dA[i])) return QLORA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_dA_shared_workspace_bytes(M, K, count, r))
     return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;
@@ -210,7 +212,7 @@ int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t 
   if (M < 0 || !isfinite(scale)) return QLORA_ERR_INVALID_ARG;
   if (N < 8 || N % 8 || r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > kMaxElems / N || N > kMaxElems / 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
-  if (!bf16_ok(dY) || !bf16_ok(B) || !bf16_ok(G)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(dY, M) || !bf16_ok(B) || !rows_ok(G, M)) return QLORA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grad_in_workspace_bytes(N, r)) return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_lora_grad_in(dY, static_cast<int>(M), static_cast<int>(N), B, r, scale, G, ws,
@@ -221,7 +223,7 @@ int qlora_nf4_matmul_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W
                          const uint16_t *B, int32_t r, uint16_t *Y, void *stream) {
   int st = check_linear_shape(M, W, r, 1.0f);
   if (st) return st;
-  if (!bf16_ok(X) || !bf16_ok(T) || !bf16_ok(B) || !bf16_ok(Y)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(X, M) || !rows_ok(T, M) || !bf16_ok(B) || !rows_ok(Y, M)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_matmul_fwd(X, static_cast<int>(M), view_of(W), T, B, r, Y,
                                     static_cast<hipStream_t>(stream)));
@@ -231,7 +233,7 @@ int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W
                         const uint16_t *A, int32_t r, uint16_t *dX, void *stream) {
   int st = check_linear_shape(M, W, r, 1.0f);
   if (st) return st;
-  if (!bf16_ok(dY) || !bf16_ok(G) || !bf16_ok(A) || !bf16_ok(dX)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(dY, M) || !rows_ok(G, M) || !bf16_ok(A) || !rows_ok(dX, M)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_matmul_dx(dY, static_cast<int>(M), view_of(W), G, A, r, dX,
                                    static_cast<hipStream_t>(stream)));
@@ -251,8 +253,8 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
   if ((dA && (K < 8 || K % 8)) || (dB && (N < 8 || N % 8))) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (M > 0 && M > kMaxElems / std::max(N, K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
   if (!bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
-  if (dA && (!bf16_ok(X) || !bf16_ok(G))) return QLORA_ERR_INVALID_ARG;
-  if (dB && (!bf16_ok(dY) || !bf16_ok(T))) return QLORA_ERR_INVALID_ARG;
+  if (dA && (!rows_ok(X, M) || !rows_ok(G, M))) return QLORA_ERR_INVALID_ARG;
+  if (dB && (!rows_ok(dY, M) || !rows_ok(T, M))) return QLORA_ERR_INVALID_ARG;
   const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grads_workspace_bytes(M, N, K, r))
     return QLORA_ERR_WORKSPACE;
@@ -276,7 +278,7 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
                      size_t ws_bytes, void *stream) {
   int st = check_linear_shape(M, W, r, scale);
   if (st) return st;
-  if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B) || !bf16_ok(Y) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(X, M) || !bf16_ok(A) || !bf16_ok(B) || !rows_ok(Y, M) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
   if (small_m_ok(M, r)) {
     if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->rows, W->cols, r)) return QLORA_ERR_WORKSPACE;
     SmGroup grp{};
@@ -295,11 +297,11 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
     return from_hip(launch_small_m(grp, static_cast<hipStream_t>(stream)));
   }
   uint16_t *T = T_out;
-  if (!T) {
+  if (!T && M > 0) {
     if (!ws || !aligned(ws, 16) || ws_bytes < fwd_ws(M, W->rows, W->cols, r)) return QLORA_ERR_WORKSPACE;
     T = static_cast<uint16_t *>(ws);
   }
-  if (M == 0) return QLORA_OK;
+  if (M == 0) return QLORA_OK;   // no workspace is needed (its size query gives 0)
   hipStream_t s = static_cast<hipStream_t>(stream);
   const NF4View v = view_of(W);
   const int m = static_cast<int>(M);
@@ -339,7 +341,7 @@ int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, voi
     if (!d[i].W) return QLORA_ERR_INVALID_ARG;
     int st = check_linear_shape(M, d[i].W, d[i].r, d[i].scale);
     if (st) return st;
-    if (!bf16_ok(d[i].X) || !bf16_ok(d[i].A) || !bf16_ok(d[i].B) || !bf16_ok(d[i].Y) || !bf16_opt(d[i].T_out))
+    if (!rows_ok(d[i].X, M) || !bf16_ok(d[i].A) || !bf16_ok(d[i].B) || !rows_ok(d[i].Y, M) || !bf16_opt(d[i].T_out))
       return QLORA_ERR_INVALID_ARG;
   }
   const size_t need = qlora_linear_group_workspace_bytes(count, d, M);
@@ -421,7 +423,7 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
                      uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
   int st = check_linear_shape(M, W, r, scale);
   if (st) return st;
-  if (!bf16_ok(dY) || !bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(dY, M) || !rows_ok(X, M) || !bf16_ok(A) || !bf16_ok(B)) return QLORA_ERR_INVALID_ARG;
   if (!bf16_opt(T) || !bf16_opt(dX) || !bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
   const BwdWs L = bwd_ws(M, W->rows, W->cols, r);
   if (!ws || !aligned(ws, 16) || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
@@ -473,7 +475,7 @@ int qlora_dropout_mask(const uint16_t *X, int64_t M, int64_t K, float p, uint64_
                        uint32_t *keep, void *stream) {
   if (M < 0 || !drop_p_ok(p)) return QLORA_ERR_INVALID_ARG;
   if (K < 32 || K % 32 || (M > 0 && M > kMaxElems / K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
-  if (!bf16_ok(X) || !bf16_ok(X_drop) || !keep || !aligned(keep, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(X, M) || !rows_ok(X_drop, M) || !rows_ok(keep, M)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_dropout_mask(X, M * K, seed, drop_thresh(p), X_drop, keep, static_cast<hipStream_t>(stream)));
 }
@@ -482,7 +484,7 @@ int qlora_dropout_apply(const uint16_t *X, int64_t M, int64_t K, const uint32_t 
                         void *stream) {
   if (M < 0) return QLORA_ERR_INVALID_ARG;
   if (K < 32 || K % 32 || (M > 0 && M > kMaxElems / K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
-  if (!bf16_ok(X) || !bf16_ok(X_drop) || !keep || !aligned(keep, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(X, M) || !rows_ok(X_drop, M) || !rows_ok(keep, M)) return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_dropout_apply(X, M * K, keep, X_drop, static_cast<hipStream_t>(stream)));
 }
@@ -491,7 +493,7 @@ int qlora_nf4_matmul_dx_dropout(const uint16_t *dY, int64_t M, const qlora_nf4_w
                                 const uint16_t *A, int32_t r, const uint32_t *keep, uint16_t *dX, void *stream) {
   int st = check_linear_shape(M, W, r, 1.0f);
   if (st) return st;
-  if (!bf16_ok(dY) || !bf16_ok(G) || !bf16_ok(A) || !bf16_ok(dX) || !keep || !aligned(keep, 16))
+  if (!rows_ok(dY, M) || !rows_ok(G, M) || !bf16_ok(A) || !rows_ok(dX, M) || !rows_ok(keep, M))
     return QLORA_ERR_INVALID_ARG;
   if (M == 0) return QLORA_OK;
   return from_hip(launch_matmul_dx_drop(dY, static_cast<int>(M), view_of(W), G, A, r, keep, dX,
@@ -511,8 +513,8 @@ int qlora_linear_fwd_dropout(const uint16_t *X, int64_t M, const qlora_nf4_weigh
   int st = check_linear_shape(M, W, r, scale);
   if (st) return st;
   if (!drop_p_ok(p)) return QLORA_ERR_INVALID_ARG;
-  if (!bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B) || !bf16_ok(Y) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
-  if (!keep_out || !aligned(keep_out, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(X, M) || !bf16_ok(A) || !bf16_ok(B) || !rows_ok(Y, M) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(keep_out, M)) return QLORA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_linear_dropout_workspace_bytes(M, W->rows, W->cols, r, 0))
     return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;
@@ -534,9 +536,9 @@ int qlora_linear_bwd_dropout(const uint16_t *dY, const uint16_t *X, const uint16
   int st = check_linear_shape(M, W, r, scale);
   if (st) return st;
   if (!drop_p_ok(p)) return QLORA_ERR_INVALID_ARG;
-  if (!bf16_ok(dY) || !bf16_ok(X) || !bf16_ok(A) || !bf16_ok(B)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(dY, M) || !rows_ok(X, M) || !bf16_ok(A) || !bf16_ok(B)) return QLORA_ERR_INVALID_ARG;
   if (!bf16_opt(T) || !bf16_opt(dX) || !bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
-  if (!keep || !aligned(keep, 16)) return QLORA_ERR_INVALID_ARG;
+  if (!rows_ok(keep, M)) return QLORA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_linear_dropout_workspace_bytes(M, W->rows, W->cols, r, 1))
     return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;

@@ -35,7 +35,9 @@
  *  - Gradients overwrite their outputs (no accumulation).
  *  - M = 0 (no tokens) is valid everywhere a token count is taken: the call
  *    validates its arguments, launches nothing and writes nothing (dA and dB,
- *    which would be zero, are left as they were).
+ *    which would be zero, are left as they were).  Pointers to tensors with M
+ *    rows (X, dY, Y, T, G, dX, keep masks) may then be NULL, as the storage of
+ *    an empty tensor is.
  *  - The linear-layer calls take W [N, K] with K % 64 == 0 (a 64-block never
  *    straddles a row), N % 8 == 0 (16-byte rows of Y and dB) and every size
  *    below 2^31 (M * max(N, K) included); the codec calls take any

@@ -103,6 +103,16 @@ int main(void) {
   EXPECT(qlora_lora_grad_in(PH, 4, 64, PH, 8, 1.0f, OH, NULL, 0, NULL), QLORA_ERR_WORKSPACE);
   EXPECT(qlora_lora_grads(PH, PH, PH, PH, 4, 64, 64, 8, OH, OH, NULL, 0, NULL), QLORA_ERR_WORKSPACE);
   EXPECT(qlora_lora_grads(PH, PH, PH, PH, 0, 64, 64, 8, OH, OH, P, BIG, NULL), QLORA_OK);
+  /* M = 0: tensors with M rows may be NULL (empty storage), workspace-free forward */
+  EXPECT(qlora_linear_fwd(NULL, 0, &w, PH, PH, 8, 1.0f, NULL, NULL, NULL, 0, NULL), QLORA_OK);
+  EXPECT(qlora_linear_bwd(NULL, NULL, NULL, 0, &w, PH, PH, 8, 1.0f, NULL, OH, OH, P, BIG, NULL), QLORA_OK);
+  EXPECT(qlora_lora_grads(NULL, NULL, NULL, NULL, 0, 64, 64, 8, OH, OH, P, BIG, NULL), QLORA_OK);
+  EXPECT(qlora_lora_down(NULL, 0, 64, PH, 8, 1.0f, NULL, NULL), QLORA_OK);
+  EXPECT(qlora_nf4_matmul_fwd(NULL, 0, &w, NULL, PH, 8, NULL, NULL), QLORA_OK);
+  EXPECT(qlora_dropout_mask(NULL, 0, 64, 0.1f, 1, NULL, NULL, NULL), QLORA_OK);
+  EXPECT(qlora_linear_fwd(NULL, 8, &w, PH, PH, 8, 1.0f, OH, OH, P, BIG, NULL), QLORA_ERR_INVALID_ARG);
+  EXPECT(qlora_linear_bwd(PH, PH, NULL, 0, &w, NULL, PH, 8, 1.0f, NULL, OH, OH, P, BIG, NULL),
+         QLORA_ERR_INVALID_ARG);   /* A has r rows, not M: never NULL */
 
   /* grouped forward: descriptors read on the host */
   qlora_linear_desc d[9];
