@@ -15,11 +15,13 @@ QLORA_ERR_INVALID_ARG = -1
 QLORA_ERR_UNSUPPORTED_SHAPE = -2
 QLORA_ERR_WORKSPACE = -3
 QLORA_ERR_HIP = -4
+QLORA_ERR_SCRATCH_LIMIT = -5
+STATIC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
     "qlora_status_string", "qlora_version", "qlora_nf4_sizes",
     "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_quantize_nf4_16", "qlora_dequantize_nf4",
-    "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
+    "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_bwd",
     "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in_workspace_bytes", "qlora_lora_grad_in",
     "qlora_nf4_matmul_dx",
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
@@ -76,6 +78,7 @@ _SIGS = {
     "qlora_dequantize_nf4": (ctypes.c_int, [_wp, _vp, _vp]),
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, ctypes.c_int]),
     "qlora_linear_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp]),
     "qlora_linear_bwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
     "qlora_lora_down": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp]),

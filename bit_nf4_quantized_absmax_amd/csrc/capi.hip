@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/qlora.h"
 #include "launch.h"
@@ -88,6 +89,36 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 
 }  // namespace
 
+// ---- static device scratch (qlora_linear_fwd_noalloc) -------------------------
+// One file-scope device array per GPU, allocated when the library's code object
+// is loaded on that GPU and held until the process ends.  Its host-side name
+// is only a handle: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is ever
+// passed to kernels.
+static __device__ __align__(256) uint8_t scratch[QLORA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int current_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return QLORA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *qlora_status_string(int status) {
@@ -98,6 +129,9 @@ const char *qlora_status_string(int status) {
       return "QLORA_ERR_UNSUPPORTED_SHAPE: need K % 64 == 0, N % 8 == 0, 1 <= r <= 128, sizes < 2^31";
     case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
     case QLORA_ERR_HIP: return "QLORA_ERR_HIP: HIP runtime or launch failure";
+    case QLORA_ERR_SCRATCH_LIMIT:
+      return "QLORA_ERR_SCRATCH_LIMIT: the call needs more than the library's static scratch "
+             "(QLORA_STATIC_SCRATCH_BYTES); pass T_out or use the workspace entry point";
     default: return "QLORA: unknown status";
   }
 }
@@ -308,6 +342,26 @@ int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, co
   hipError_t e = launch_lora_down(X, m, v.K, A, r, scale, T, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   return from_hip(launch_matmul_fwd(X, m, v, T, B, r, Y, s));
+}
+
+int qlora_linear_fwd_noalloc(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *A,
+                             const uint16_t *B, int32_t r, float scale, uint16_t *Y, uint16_t *T_out,
+                             void *stream) {
+  int st = check_linear_shape(M, W, r, scale);
+  if (st) return st;
+  if (!rows_ok(X, M) || !bf16_ok(A) || !bf16_ok(B) || !rows_ok(Y, M) || !bf16_opt(T_out)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  // The workspace qlora_linear_fwd would use: the decode-regime partials, or T
+  // when the caller keeps no T_out.  Nothing in it has to start at zero: every
+  // byte the kernels read was written earlier in the same call.
+  const size_t need = (small_m_ok(M, r) || !T_out) ? fwd_ws(M, W->rows, W->cols, r) : 0;
+  if (need > QLORA_STATIC_SCRATCH_BYTES) return QLORA_ERR_SCRATCH_LIMIT;
+  void *ptr = nullptr;
+  if (need) {
+    st = current_scratch(&ptr);
+    if (st) return st;
+  }
+  return qlora_linear_fwd(X, M, W, A, B, r, scale, Y, T_out, ptr, need ? QLORA_STATIC_SCRATCH_BYTES : 0, stream);
 }
 
 static bool group_small_m(int count, const qlora_linear_desc *d, int64_t M) {

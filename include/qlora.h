@@ -61,8 +61,12 @@ typedef enum {
   QLORA_ERR_INVALID_ARG = -1,       /* null/misaligned pointer, negative size, bad scale */
   QLORA_ERR_UNSUPPORTED_SHAPE = -2, /* K % 64 != 0, N % 8 != 0, r outside [1, 128], size >= 2^31 */
   QLORA_ERR_WORKSPACE = -3,         /* workspace missing or smaller than required */
-  QLORA_ERR_HIP = -4                /* a HIP runtime call or kernel launch failed */
+  QLORA_ERR_HIP = -4,               /* a HIP runtime call or kernel launch failed */
+  QLORA_ERR_SCRATCH_LIMIT = -5      /* qlora_linear_fwd_noalloc: needs more than the static scratch */
 } qlora_status;
+
+/* Size of the per-GPU static scratch array of qlora_linear_fwd_noalloc. */
+#define QLORA_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* 4-bit data types of the first-level codes: the 16-entry level table the
  * codes index.  Everything else in the format (blocks of 64, nearest level
@@ -180,6 +184,27 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, 
 int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
                      const uint16_t *A, const uint16_t *B, int32_t r, float scale,
                      uint16_t *Y, uint16_t *T_out, void *ws, size_t ws_bytes, void *stream);
+
+/* qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, rules and results as
+ * qlora_linear_fwd (bit for bit: the same kernels); its scratch is a static
+ * device array of QLORA_STATIC_SCRATCH_BYTES (16 MiB) per GPU, created when
+ * the library is first used on that GPU and held until the process ends.
+ * The call allocates nothing and calls no allocating routine.
+ *   - Scratch needed: the decode-regime partials at 1 <= M <= 64 (r % 8 ==
+ *     0; at most 13.4 MiB for the LLaMA-7B..65B shapes) or T [M, r] bf16
+ *     when T_out is NULL.  A call that needs more returns
+ *     QLORA_ERR_SCRATCH_LIMIT before launching anything.
+ *   - The scratch of the current device is used: `stream` must belong to it.
+ *   - Calls on one GPU share its scratch, which keeps the last call's
+ *     contents (nothing in it needs clearing between calls).  Calls ordered
+ *     on one stream are safe; calls that can overlap in time on the same GPU
+ *     (different streams, several host threads) race on it and must be
+ *     ordered by the caller. */
+int qlora_linear_fwd_noalloc(const uint16_t *X, int64_t M, const qlora_nf4_weight *W,
+                             const uint16_t *A, const uint16_t *B, int32_t r, float scale,
+                             uint16_t *Y, uint16_t *T_out, void *stream);
 
 /* One linear of a grouped forward call (all pointers device memory, same
  * layouts and rules as qlora_linear_fwd). */

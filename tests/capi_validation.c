@@ -114,6 +114,13 @@ int main(void) {
   EXPECT(qlora_linear_bwd(PH, PH, NULL, 0, &w, NULL, PH, 8, 1.0f, NULL, OH, OH, P, BIG, NULL),
          QLORA_ERR_INVALID_ARG);   /* A has r rows, not M: never NULL */
 
+  /* the static-scratch forward: rejections and M = 0 happen before any HIP call */
+  qlora_nf4_weight w64 = fake_weight(64, 64, QLORA_Q4_NF4);
+  EXPECT(qlora_linear_fwd_noalloc(PH, 70000, &w64, PH, PH, 128, 1.0f, OH, NULL, NULL), QLORA_ERR_SCRATCH_LIMIT);
+  EXPECT(qlora_linear_fwd_noalloc(PH, 8, &wk, PH, PH, 8, 1.0f, OH, NULL, NULL), QLORA_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(qlora_linear_fwd_noalloc(NULL, 0, &w64, PH, PH, 8, 1.0f, NULL, NULL, NULL), QLORA_OK);
+  EXPECT_TRUE(qlora_status_string(QLORA_ERR_SCRATCH_LIMIT)[0] != 0);
+
   /* grouped forward: descriptors read on the host */
   qlora_linear_desc d[9];
   for (int i = 0; i < 9; ++i) {

@@ -213,3 +213,15 @@ def test_zero_tokens_validate_and_return_ok():
     w = _fake_weight(64, 64)
     assert L.qlora_linear_fwd_dropout(P, 0, ctypes.byref(w), P, P, 8, 1.0, 0.1, 1, P, None, P, P, 1 << 20,
                                       None) == OK
+
+
+def test_noalloc_forward_validates_before_touching_the_gpu():
+    L = q.lib()
+    P = ctypes.c_void_p(0x20000)
+    w = _fake_weight(64, 64)
+    # T [70000, 128] bf16 does not fit the 16 MiB static scratch without T_out
+    assert L.qlora_linear_fwd_noalloc(P, 70000, ctypes.byref(w), P, P, 128, 1.0, P, None, None) == -5
+    assert L.qlora_linear_fwd_noalloc(P, 8, ctypes.byref(_fake_weight(64, 100)), P, P, 8, 1.0, P, None, None) == SHAPE
+    assert L.qlora_linear_fwd_noalloc(None, 0, ctypes.byref(w), P, P, 8, 1.0, None, None, None) == OK
+    assert "SCRATCH" in q.status_string(-5)
+    assert _capi.STATIC_SCRATCH_BYTES == 16 << 20
