@@ -68,6 +68,8 @@ def parse():
                    help="only the small-M (decode) figures, as one JSON line (for profiling that path)")
     p.add_argument("--small-m-eager", action="store_true",
                    help="with --small-m-only: eager calls instead of graph replays (counter passes)")
+    p.add_argument("--codec-only", action="store_true",
+                   help="only the quantize / dequantize figures, as one JSON line (for profiling the codec)")
     p.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB first (a reference "
@@ -295,26 +297,60 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True):
     return out
 
 
-def quantize_bench(q, torch, workloads, cfg, dev, reps=5):
-    Ws = [workloads.device_normal((l.out_features, l.in_features), workloads.W_STD, 95000 + i, dev)
-          for i, l in enumerate(cfg.linears)]
-    for W in Ws:
-        q.NF4Weight.quantize(W)
+def quantize_bench(q, torch, workloads, cfg, dev, reps=10):
+    """Quantization (fp32 weights -> packed codes + double-quantized
+    constants) of the 7 weights of a layer, over 4 weight sets (> the 256 MB
+    Infinity Cache), through the C ABI with preallocated outputs and
+    workspaces, captured once in a HIP graph and replayed.  Algorithmic bytes
+    per parameter: 4 (fp32) read, 1/2 (codes) + 1/64 (constant codes) +
+    4/16384 (group scales) written."""
+    import ctypes
+    lib = q.lib()
+    sets = []
+    for si in range(4):
+        items = []
+        for li, lin in enumerate(cfg.linears):
+            rows, cols = lin.out_features, lin.in_features
+            W = workloads.device_normal((rows, cols), workloads.W_STD, 95000 + 100 * si + li, dev)
+            w = q.NF4Weight.empty(rows, cols, W.device)
+            nws = lib.qlora_quantize_workspace_bytes(rows * cols)
+            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+            items.append((W, w, w.struct(), ws, nws))
+        sets.append(items)
+
+    def run(stream):
+        for items in sets:
+            for W, _, st, ws, nws in items:
+                rc = lib.qlora_quantize_nf4(W.data_ptr(), ctypes.byref(st), ws.data_ptr(), nws, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("qlora_quantize_nf4 failed: %d" % rc)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run(stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        for W in Ws:
-            q.NF4Weight.quantize(W)
-    e1.record()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run(stream)
+    for _ in range(3):
+        graph.replay()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    params = sum(W.numel() for W in Ws)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record()
+    for i in range(reps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / 4 for i in range(reps))
+    us = evs[0].elapsed_time(evs[-1]) * 1e3 / (4 * reps)
+    params = sum(l.out_features * l.in_features for l in cfg.linears)
     nbytes = params * (4 + 0.5 + 1 / 64 + 4 / 16384)
-    del Ws
+    del graph, sets
     torch.cuda.empty_cache()
-    return dict(ms_per_layer=round(ms, 3), params=int(params), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
-                note="includes workspace allocation by the Python binding")
+    return dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
+                params=int(params), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                launches_per_layer=2 * len(cfg.linears))
 
 
 def q4_types_bench(q, torch, workloads, dev, reps=10):
@@ -658,6 +694,12 @@ def main():
                            graphs=not args.small_m_eager)
         print(json.dumps(dict(metric="small-M dequant forward GB/s (7B layer, 7 linears, 4 weight sets)",
                               unit="GB/s", data="synthetic", small_m=sm)), flush=True)
+        return
+    if args.codec_only:
+        c1 = workloads.CONFIGS[1]
+        print(json.dumps(dict(metric="NF4 codec GB/s (7B layer, 7 weights, 4 weight sets)", unit="GB/s",
+                              data="synthetic", quantize=quantize_bench(q, torch, workloads, c1, dev),
+                              dequantize=dequantize_bench(q, torch, workloads, c1, dev))), flush=True)
         return
     cfg = workloads.CONFIGS[1]
     scale = cfg.scale
