@@ -68,6 +68,8 @@ def parse():
                    help="only the small-M (decode) figures, as one JSON line (for profiling that path)")
     p.add_argument("--small-m-eager", action="store_true",
                    help="with --small-m-only: eager calls instead of graph replays (counter passes)")
+    p.add_argument("--small-m-pattern", choices=("both", "grouped", "per_linear"), default="both",
+                   help="with --small-m-only: the launch patterns to run (profiles of one pattern)")
     p.add_argument("--codec-only", action="store_true",
                    help="only the quantize / dequantize figures, as one JSON line (for profiling the codec)")
     p.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle")
@@ -201,7 +203,7 @@ def cpu_baseline(cfg, tokens):
                        "tokens, %.1f s; rate = algorithmic FLOP / time" % (tokens, total_s))
 
 
-def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True):
+def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True, patterns=("per_linear", "grouped")):
     """Forward at M = 1/16/64 over 4 weight sets of the 7B layer (> Infinity Cache).
 
     Two launch patterns, each captured once in a HIP graph and replayed (the
@@ -258,6 +260,8 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True):
 
         res = {}
         for name, fn in (("per_linear", lambda si: per_linear(sets[si])), ("grouped", grouped)):
+            if name not in patterns:
+                continue
             for si in range(len(sets)):
                 fn(si)
             torch.cuda.synchronize()
@@ -288,8 +292,10 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True):
             res[name] = dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
                              reps=reps, GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
             del graph
-        res["per_linear"]["launches_per_layer"] = (2 if M <= 16 else 4) * len(cfg.linears)
-        res["grouped"]["launches_per_layer"] = 2 if M <= 4 else 4
+        if "per_linear" in res:
+            res["per_linear"]["launches_per_layer"] = (2 if M <= 16 else 4) * len(cfg.linears)
+        if "grouped" in res:
+            res["grouped"]["launches_per_layer"] = 2 if M <= 4 else 4
         res["bytes_per_layer"] = int(nbytes)
         out["M%d" % M] = res
     del sets
@@ -350,7 +356,7 @@ def quantize_bench(q, torch, workloads, cfg, dev, reps=10):
     return dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
                 params=int(params), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
                 frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                launches_per_layer=2 * len(cfg.linears))
+                launches_per_layer=3 * len(cfg.linears))
 
 
 def q4_types_bench(q, torch, workloads, dev, reps=10):
@@ -690,8 +696,9 @@ def main():
         torch.cuda.empty_cache()
     if args.small_m_only:
         c2 = workloads.CONFIGS[2]
+        pats = ("per_linear", "grouped") if args.small_m_pattern == "both" else (args.small_m_pattern,)
         sm = small_m_bench(q, torch, workloads, c2, dev, reps=5 if args.small_m_eager else 200,
-                           graphs=not args.small_m_eager)
+                           graphs=not args.small_m_eager, patterns=pats)
         print(json.dumps(dict(metric="small-M dequant forward GB/s (7B layer, 7 linears, 4 weight sets)",
                               unit="GB/s", data="synthetic", small_m=sm)), flush=True)
         return
