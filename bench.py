@@ -747,7 +747,9 @@ def main():
     dom_kernel = "qlora::k_matmul<false, false>" if dom_key == "fwd" else "qlora::k_matmul<true, false>"
     roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=recorded_traffic(dom_kernel),
-                    traffic_unit="HBM bytes per launch (PMC FETCH_SIZE/WRITE_SIZE, copy-scaled)",
+                    traffic_unit="HBM bytes per launch (PMC FETCH_SIZE + WRITE_SIZE, copy-scaled), recorded in "
+                                 "profiles/matmul_llama7b_m8192_hbm_traffic.md, not measured by this run; null "
+                                 "once the matmul sources differ from the recorded hash",
                     kernel=dom_kernel + (" (forward)" if dom_key == "fwd" else " (dX)"),
                     avg_launch_us=round(dom["avg_us"], 2),
                     flops_per_launch=dom["flops_per_launch"])
