@@ -356,7 +356,7 @@ def quantize_bench(q, torch, workloads, cfg, dev, reps=10):
     return dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
                 params=int(params), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
                 frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                launches_per_layer=3 * len(cfg.linears))
+                launches_per_layer=2 * len(cfg.linears))
 
 
 def q4_types_bench(q, torch, workloads, dev, reps=10):

@@ -3,16 +3,19 @@
 // Quantize (automatone.win, "QLoRA paper explained", How it works / 4-bit
 // NormalFloat and Double Quantization; creativeworksofknowledge.com, "QLoRA:
 // Fine-Tune 70B on One GPU", The three innovations / 1-2):
-//   pass 1  k_quant_blocks   one read of W: per-64 absmax, NF4 codes, nibbles
-//   pass 2  k_tree_sum       fp64 pairwise tree of the absmax values (fixed
-//                            order, levels of aligned 2048-chunks until at
-//                            most 2048 partials remain)
-//   pass 3  k_quant_consts   last tree level, mean, per-256 scale c2, 8-bit
-//                            constant codes
+//   pass 1  k_quant_blocks   one read of W: per-64 absmax, 4-bit codes,
+//                            nibbles, and the fp64 sum of each workgroup's
+//                            256 absmax values (one aligned subtree of the
+//                            pairwise sum tree)
+//   pass 2  k_quant_consts   the rest of the tree, mean, per-256 scale c2,
+//                            8-bit constant codes
+//   (k_tree_sum runs between them only when more than 8192 subtree sums
+//   remain, i.e. for weights over 2^27 elements.)
 // Dequantize: k_dequant     packed codes -> bf16, one read, one write.
 //
-// Bit-exactness rules: fp32 division is IEEE correctly rounded (hipcc's
-// default), no fused multiply-add (-ffp-contract=off), bf16 conversion is
+// Bit-exactness rules: the 4-bit code of w is the count of table thresholds
+// strictly below x = fl32(w / absmax) (IEEE quotient, correctly rounded); no
+// fused multiply-add (-ffp-contract=off), bf16 conversion is
 // round-to-nearest-even, the tree order is fixed.
 #include "common.h"
 #include "launch.h"
@@ -27,119 +30,235 @@ __constant__ uint32_t cT8Thresh[255] = {QLORA_T8_THRESH_BITS};
 constexpr int kTreeChunk = 2048;   // elements reduced by one workgroup of k_tree_sum
 constexpr int kThreads = 256;
 
-// Nearest level of a 4-bit table, ties to the lower code: the number of its 15
-// ascending thresholds (th, in LDS) strictly below x, by a 4-step binary
-// search (equal thresholds, as FP4's two zero levels give, are counted alike).
-__device__ __forceinline__ uint32_t q4_code(float x, const float *th) {
-  uint32_t q = (x > th[7]) ? 8u : 0u;
-  q += (x > th[q + 3]) ? 4u : 0u;
-  q += (x > th[q + 1]) ? 2u : 0u;
-  q += (x > th[q]) ? 1u : 0u;
-  return q;
-}
-
 // ---------------------------------------------------------------------------
-// Pass 1.  Each lane owns 4 consecutive elements; 16 lanes form one block of
-// 64.  The lane group reduces |w| with cross-lane max, every lane divides its
-// elements by the block absmax and codes them, and writes its 2 packed bytes.
-// Elements past n do not exist: they do not enter the max and pack as 0.
+// Pass 1.  Workgroup w owns blocks [256 w, 256 w + 256), i.e. elements
+// [16384 w, 16384 w + 16384).  Thread t loads all of its 16 chunks of 4
+// consecutive elements (chunk i = elements 16384 w + 1024 i + 4 t ..) before
+// coding the first, so each thread keeps 16 loads in flight; the 16 lanes
+// t = 16 g .. 16 g + 15 of chunk i form block 16 i + g.  Elements past n do not
+// exist: they load as 0 (which cannot raise a maximum of |w|) and pack as 0.
 // The input is fp32 (kIn = 0) or 16-bit bit patterns, bf16 (1) or fp16 (2),
 // which widen to fp32 exactly, so every input type codes its fp32 value.
+//
+// Coding without a division per element.  Multiplying x by 16 is exact, so
+// the code is the count of thresholds tau with 16 tau < 16 x.  Cell k
+// (k = -16..16) covers 16 x in [k - 1/2, k + 1/2) and stores the count lo of
+// thresholds below the cell, the count of thresholds inside it (1, 2 for a
+// repeated value, or 0) and 16 tau of the one threshold value inside it
+// (+inf if none).  Every threshold of every table lies at least 2^-4 (in
+// 16 x units) from a cell edge; a compile-time check below enforces it.
+// The kernel forms y = w * fl32(16 * rcp(a)); for a >= 2^-100 (rcp accurate
+// to 1 ulp, two more roundings) |y - 16 x| < 2^-17.  The cell is taken from
+// y and the code is lo, plus the inside count if y > 16 tau.  This equals the
+// exact code whenever |y - 16 tau| >= 2^-15: then y and 16 x lie on the same
+// side of 16 tau, and any cell edge between them has no threshold within
+// 2^-4 of it.  If one lane of the wave is closer than 2^-15 to its cell's
+// threshold, or one block of the wave has a < 2^-100, the wave recodes that
+// chunk from the correctly rounded quotient x = w / a, with the same cells.
+// Codes of non-finite weights are unspecified (table indices stay clamped).
 // ---------------------------------------------------------------------------
-template <int kIn>
-__device__ __forceinline__ float widen(const void *W, int64_t i) {
-  if (kIn == 0) return static_cast<const float *>(W)[i];
-  const uint16_t h = static_cast<const uint16_t *>(W)[i];
-  if (kIn == 1) return u2f(static_cast<uint32_t>(h) << 16);
-  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+constexpr int kWgBlocks = 256;                           // blocks per workgroup of pass 1
+constexpr int kWgElems = kWgBlocks * kBlock;             // 16384 elements
+constexpr int kChunks = kWgElems / (kThreads * 4);       // 16 chunks of 4 per thread
+constexpr int kCellUnit = 16;                            // cells per unit of x
+constexpr int kCells = 2 * kCellUnit + 1;                // x in [-1, 1]
+constexpr float kNearBand = 0x1p-15f;                    // |y - 16 tau| below this: exact recode
+constexpr float kTinyAbsmax = 0x1p-100f;                 // below this: exact recode
+
+// Compile-time check of the cell property for the three 4-bit tables: each
+// threshold at least 2^-4 from a cell edge (in 16 x units), ascending order.
+constexpr double q4_threshold_value(uint32_t bits) {
+  return static_cast<double>(__builtin_bit_cast(float, bits));
+}
+constexpr bool q4_cells_separate() {
+  constexpr uint32_t th[3 * 15] = {QLORA_Q4_THRESH_BITS};
+  for (int q = 0; q < 3; ++q) {
+    for (int i = 0; i < 15; ++i) {
+      const double y = 16.0 * q4_threshold_value(th[15 * q + i]);
+      if (i > 0 && q4_threshold_value(th[15 * q + i]) < q4_threshold_value(th[15 * q + i - 1])) return false;
+      double edge = static_cast<double>(static_cast<long long>(y < 0 ? y - 1.0 : y)) + 0.5;   // floor(y) + 1/2
+      const double d0 = y - (edge - 1.0), d1 = edge - y, d2 = (edge + 1.0) - y;
+      const double d = (d0 < 0 ? -d0 : d0) < (d1 < 0 ? -d1 : d1) ? (d0 < 0 ? -d0 : d0) : (d1 < 0 ? -d1 : d1);
+      if ((d < (d2 < 0 ? -d2 : d2) ? d : (d2 < 0 ? -d2 : d2)) < 0.0625) return false;
+    }
+  }
+  return true;
+}
+static_assert(q4_cells_separate(), "4-bit thresholds too close to a coding cell edge");
+
+// Cell table of table qtype into c[0 .. kCells): (bits of 16 tau or +inf, lo | hi << 16).
+__device__ __forceinline__ void build_cells(int qtype, uint2 *c) {
+  const int t = threadIdx.x;
+  if (t < kCells) {
+    const int k = t - kCellUnit;
+    const float lo = (k - 0.5f) / kCellUnit, hi = (k + 0.5f) / kCellUnit;   // exact: odd / 32
+    uint32_t below = 0, inside = 0;
+    float tau16 = INFINITY;
+    for (int i = 0; i < 15; ++i) {
+      const float th = u2f(cQ4Thresh[15 * qtype + i]);
+      below += th < lo;
+      if (th >= lo && th < hi) { ++inside; tau16 = th * 16.0f; }
+    }
+    c[t] = make_uint2(__float_as_uint(tau16), below | ((below + inside) << 16));
+  }
 }
 
-constexpr int kQU = 2;   // 4-element chunks per thread per pass of k_quant_blocks
+// Cell of 16 x from y = 16 x (approximately): nearest integer, clamped.
+__device__ __forceinline__ int cell_index(float y) {
+  int k;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(k) : "v"(y));   // floor(y + 1/2); NaN -> 0
+  return min(max(k, -kCellUnit), kCellUnit);
+}
+
+// Maximum over the 16 lanes of a row (one block): non-negative floats order
+// as their bit patterns.
+__device__ __forceinline__ float row16_max(float a) {
+  uint32_t u = __float_as_uint(a);
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0xB1, 0xF, 0xF, false)));   // lane ^ 1
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x4E, 0xF, 0xF, false)));   // lane ^ 2
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x141, 0xF, 0xF, false)));  // half mirror
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x140, 0xF, 0xF, false)));  // mirror
+  return __uint_as_float(u);
+}
 
 template <int kIn>
-__device__ __forceinline__ void load_chunk(const void *W, int64_t e, int64_t n, float w[4]) {
-  if (e + 3 < n && kIn == 0) {
-    typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(static_cast<const float *>(W) + e));
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else if (e + 3 < n) {
-    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(W) + e));
-    const uint32_t hs[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+__device__ __forceinline__ float widen16(uint32_t h) {
+  return kIn == 1 ? u2f(h << 16) : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// Raw chunk storage: 4 fp32 values, or 4 16-bit patterns in two dwords.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <int kIn> struct RawChunk { typedef u32x2_t type; };
+template <> struct RawChunk<0> { typedef f32x4_t type; };
+
+template <int kIn>
+__device__ __forceinline__ f32x4_t widen_chunk(const typename RawChunk<kIn>::type &r) {
+  if constexpr (kIn == 0) {
+    return r;
+  } else {
+    f32x4_t v;
+    v[0] = widen16<kIn>(r.x & 0xFFFFu);
+    v[1] = widen16<kIn>(r.x >> 16);
+    v[2] = widen16<kIn>(r.y & 0xFFFFu);
+    v[3] = widen16<kIn>(r.y >> 16);
+    return v;
+  }
+}
+
+// The 16 chunks of one thread, coded; kFull: the workgroup's range lies wholly below n.
+template <int kIn, bool kFull>
+__device__ __forceinline__ void quant_chunks(const void *__restrict__ W, int64_t n, int qtype,
+                                             uint8_t *__restrict__ packed, const uint2 *cells, float *sA) {
+  typedef typename RawChunk<kIn>::type raw_t;
+  const int t = threadIdx.x;
+  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kWgElems;
+  raw_t r[kChunks];
+  if (kFull) {
+    const raw_t *src = reinterpret_cast<const raw_t *>(static_cast<const char *>(W) + e0 * (kIn == 0 ? 4 : 2)) + t;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = kIn == 1 ? u2f(hs[i] << 16)
-                      : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hs[i])));
+    for (int i = 0; i < kChunks; ++i) r[i] = __builtin_nontemporal_load(src + i * kThreads);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (e + i < n) ? widen<kIn>(W, e + i) : 0.0f;
+    for (int i = 0; i < kChunks; ++i) {
+      const int64_t e = e0 + static_cast<int64_t>(i * kThreads + t) * 4;
+      if constexpr (kIn == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[i][k] = (e + k < n) ? static_cast<const float *>(W)[e + k] : 0.0f;
+      } else {
+        const uint16_t *h = static_cast<const uint16_t *>(W);
+        uint32_t q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = (e + k < n) ? h[e + k] : 0u;
+        r[i] = u32x2_t{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+      }
+    }
+  }
+  __syncthreads();   // cells ready
+  const uint32_t zero_word = static_cast<uint32_t>(q4_zero_code(qtype)) * 0x1111u;
+  uint16_t *dst = reinterpret_cast<uint16_t *>(packed + (e0 >> 1));
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const f32x4_t w = widen_chunk<kIn>(r[i]);
+    const float a = row16_max(fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3]))));
+    const float r16 = 16.0f * __builtin_amdgcn_rcpf(a);
+    uint32_t word = 0;
+    bool near = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float y = w[k] * r16;
+      const uint2 ce = cells[cell_index(y)];
+      const float d = y - __uint_as_float(ce.x);
+      near |= fabsf(d) < kNearBand;
+      word |= ((ce.y >> (d > 0.0f ? 16u : 0u)) & 15u) << (4 * k);
+    }
+    if (__any(near || a < kTinyAbsmax)) {   // wave-uniform: recode from the exact quotient
+      word = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float y = (w[k] / a) * 16.0f;
+        const uint2 ce = cells[cell_index(y)];
+        word |= ((ce.y >> (y > __uint_as_float(ce.x) ? 16u : 0u)) & 15u) << (4 * k);
+      }
+    }
+    if (!(a > 0.0f)) word = zero_word;
+    if (kFull) {
+      __builtin_nontemporal_store(static_cast<uint16_t>(word), dst + i * kThreads + t);
+    } else {
+      const int64_t e = e0 + static_cast<int64_t>(i * kThreads + t) * 4;
+      if (e + 3 >= n) word &= (e >= n) ? 0u : (e + 1 >= n ? 0xFu : (e + 2 >= n ? 0xFFu : 0xFFFu));
+      if (e < n) packed[e >> 1] = static_cast<uint8_t>(word);
+      if (e + 2 < n) packed[(e >> 1) + 1] = static_cast<uint8_t>(word >> 8);
+    }
+    sA[i * 16 + (t >> 4)] = a;   // the 16 lanes of the block store the same value
   }
 }
 
-// A thread takes kQU chunks kThreads apart (a 16-lane block group stays
-// within one block) and loads all of them before coding the first; W is read
-// once, through streaming loads.
-template <int kIn>
-__global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restrict__ W, int64_t n,
-                                                           int qtype, uint8_t *__restrict__ packed,
-                                                           float *__restrict__ absmax) {
-  const uint32_t zero = static_cast<uint32_t>(q4_zero_code(qtype));
-  __shared__ float sTh[16];
-  if (threadIdx.x < 15) sTh[threadIdx.x] = u2f(cQ4Thresh[15 * qtype + threadIdx.x]);
-  __syncthreads();
-  const int64_t nchunks = ((n + kBlock - 1) / kBlock) * 16;  // 4-element chunks, whole blocks
-  const int64_t span = static_cast<int64_t>(kThreads) * kQU;
-  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x; c0 < nchunks;
-       c0 += static_cast<int64_t>(gridDim.x) * span) {
-    float w[kQU][4];
+// Pairwise fp64 sum of s[0 .. 256) by wave 0 (call after a barrier): lane l
+// forms ((s[4l] + s[4l+1]) + (s[4l+2] + s[4l+3])), then six levels pair
+// neighbouring lanes.  Returns the sum in lane 0.
+template <typename T>
+__device__ __forceinline__ double tree256_wave0(const T *s) {
+  const int l = threadIdx.x;
+  double r = (static_cast<double>(s[4 * l]) + static_cast<double>(s[4 * l + 1])) +
+             (static_cast<double>(s[4 * l + 2]) + static_cast<double>(s[4 * l + 3]));
 #pragma unroll
-    for (int u = 0; u < kQU; ++u) {
-      const int64_t c = c0 + u * kThreads;
-      if (c < nchunks) {
-        load_chunk<kIn>(W, c * 4, n, w[u]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[u][i] = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kQU; ++u) {
-      // nchunks is a multiple of 16 and a block's 16 lanes share c >> 4, so
-      // a block group is wholly in range or wholly out.
-      const int64_t c = c0 + u * kThreads;
-      if (c >= nchunks) break;
-      const int64_t e = c * 4;
-      const bool full = (e + 3 < n);
-      float a = fmaxf(fmaxf(fabsf(w[u][0]), fabsf(w[u][1])), fmaxf(fabsf(w[u][2]), fabsf(w[u][3])));
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
+  for (int w = 32; w >= 1; w >>= 1) {
+    const double lo = __shfl(r, 2 * l), hi = __shfl(r, 2 * l + 1);
+    r = lo + hi;
+  }
+  return r;
+}
 
-      uint32_t q[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        q[i] = (a > 0.0f) ? q4_code(w[u][i] / a, sTh) : zero;
-        if (e + i >= n) q[i] = 0u;
-      }
-      const uint32_t b0 = q[0] | (q[1] << 4), b1 = q[2] | (q[3] << 4);
-      uint8_t *dst = packed + (e >> 1);
-      if (full) {
-        *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(b0 | (b1 << 8));
-      } else {
-        if (e < n) dst[0] = static_cast<uint8_t>(b0);
-        if (e + 2 < n) dst[1] = static_cast<uint8_t>(b1);
-      }
-      if ((threadIdx.x & 15) == 0) absmax[c >> 4] = a;
-    }
+template <int kIn>
+__global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restrict__ W, int64_t n, int qtype,
+                                                           uint8_t *__restrict__ packed,
+                                                           float *__restrict__ absmax,
+                                                           double *__restrict__ subtree) {
+  __shared__ uint2 sCells[kCells];
+  __shared__ float sA[kWgBlocks];
+  build_cells(qtype, sCells);
+  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kWgElems;
+  if (e0 + kWgElems <= n)
+    quant_chunks<kIn, true>(W, n, qtype, packed, sCells + kCellUnit, sA);
+  else
+    quant_chunks<kIn, false>(W, n, qtype, packed, sCells + kCellUnit, sA);
+  __syncthreads();
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * kWgBlocks + threadIdx.x;
+  if (b < nb) absmax[b] = sA[threadIdx.x];
+  if (threadIdx.x < 64) {
+    const double r = tree256_wave0(sA);
+    if (threadIdx.x == 0) subtree[blockIdx.x] = r;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2.  Workgroup g reduces in[2048 g, 2048 g + 2048) (zero beyond len) to
-// one fp64 value with the neighbour-pairing tree: 8 values per thread
-// ((v0+v1)+(v2+v3))+((v4+v5)+(v6+v7)), then level by level in LDS,
-// s'[t] = s[2t] + s[2t+1].  Because chunks are aligned powers of two,
-// applying this again to the partials reproduces the global tree exactly.
-// The last level (at most 2048 partials) runs at the start of pass 3.
+// Tree levels for very large weights.  Workgroup g reduces
+// in[2048 g, 2048 g + 2048) (zero beyond len) to one fp64 value with the
+// neighbour-pairing tree: 8 values per thread ((v0+v1)+(v2+v3))+((v4+v5)+(v6+v7)),
+// then level by level in LDS, s'[t] = s[2t] + s[2t+1].  Because chunks are
+// aligned powers of two, applying this to subtree sums continues the global
+// tree exactly.
 // ---------------------------------------------------------------------------
 // Tree sum of chunk `chunk`, called by every thread of the workgroup; the
 // result is in s[0] on return (after a barrier).
@@ -170,13 +289,16 @@ __global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ i
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3.  Every workgroup first sums the last tree level (plen <= 2048
-// partials, the same tree as pass 2), then mean = fl32(sum / nb).  One wave
-// per group of 256 constants, 4 per
-// lane: d = fl32(c - mean), c2 = max |d| over the group, code = number of T8
+// Pass 2.  Every workgroup first finishes the tree over the plen <= 8192
+// subtree sums (thread t: sums 32 t .. 32 t + 31 by neighbour pairs in
+// registers, then the 256 thread sums as in tree256_wave0), then
+// mean = fl32(sum / nb).  One wave per group of 256 constants, 4 per lane:
+// d = fl32(c - mean), c2 = max |d| over the group, code = number of T8
 // thresholds below fl32(d / c2) (binary search over the 255 thresholds, with
 // +inf as a 256th sentinel).  c2 = 0 -> code 127.
 // ---------------------------------------------------------------------------
+constexpr int kConstsMaxPartials = 32 * kThreads;   // 8192
+
 __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restrict__ absmax, int64_t nb,
                                                            const double *__restrict__ partials, int64_t plen,
                                                            uint8_t *__restrict__ code8,
@@ -184,10 +306,27 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
                                                            float *__restrict__ mean_out) {
   __shared__ float thr[256];
   __shared__ double s[kThreads];
-  for (int i = threadIdx.x; i < 256; i += kThreads) thr[i] = (i < 255) ? u2f(cT8Thresh[i]) : INFINITY;
-  tree_chunk(partials, plen, 0, s);                    // ends with a barrier: thr is ready too
-  const float mean = static_cast<float>(s[0] / static_cast<double>(nb));
-  if (blockIdx.x == 0 && threadIdx.x == 0) mean_out[0] = mean;
+  __shared__ float sMean;
+  const int t = threadIdx.x;
+  for (int i = t; i < 256; i += kThreads) thr[i] = (i < 255) ? u2f(cT8Thresh[i]) : INFINITY;
+  {
+    double v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = (32 * t + i < plen) ? partials[32 * t + i] : 0.0;
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+      for (int j = 0; j < w; ++j) v[j] = v[2 * j] + v[2 * j + 1];
+    s[t] = v[0];
+  }
+  __syncthreads();
+  if (t < 64) {
+    const double r = tree256_wave0(s);
+    if (t == 0) sMean = static_cast<float>(r / static_cast<double>(nb));
+  }
+  __syncthreads();
+  const float mean = sMean;
+  if (blockIdx.x == 0 && t == 0) mean_out[0] = mean;
 
   const int lane = threadIdx.x & 63;
   const int64_t nb2 = (nb + kGroup - 1) / kGroup;
@@ -304,13 +443,15 @@ static unsigned grid_for(int64_t work_items, int64_t per_wg, int64_t cap) {
   return static_cast<unsigned>(g);
 }
 
+static int64_t subtree_count(int64_t nb) { return (nb + kWgBlocks - 1) / kWgBlocks; }
+
 size_t quantize_ws_bytes(int64_t n) {
   if (n < 1) return 0;
   const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t p1 = tree_partials(nb);
-  // absmax fp32 [nb] (padded to 256 B) | two ping-pong fp64 partial buffers [p1]
+  const int64_t p = subtree_count(nb);
+  // absmax fp32 [nb] (padded to 256 B) | subtree sums fp64 [p] | next tree level fp64 [p / 2048]
   const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
-  return a + 2 * static_cast<size_t>(p1) * 8;
+  return a + static_cast<size_t>(p + tree_partials(p)) * 8;
 }
 
 hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uint8_t *packed, uint8_t *code8,
@@ -318,30 +459,27 @@ hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uin
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
   float *absmax = static_cast<float *>(ws);
-  double *buf0 = reinterpret_cast<double *>(static_cast<char *>(ws) + a);
-  double *buf1 = buf0 + tree_partials(nb);
+  double *sub = reinterpret_cast<double *>(static_cast<char *>(ws) + a);
+  int64_t len = subtree_count(nb);
+  double *level = sub + len;
 
-  const dim3 g1(grid_for(nb * 16, kThreads * kQU, 16384));
+  const dim3 g1(static_cast<unsigned>(len));
   if (in_type == 1)
-    hipLaunchKernelGGL(k_quant_blocks<1>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
+    hipLaunchKernelGGL(k_quant_blocks<1>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax, sub);
   else if (in_type == 2)
-    hipLaunchKernelGGL(k_quant_blocks<2>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
+    hipLaunchKernelGGL(k_quant_blocks<2>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax, sub);
   else
-    hipLaunchKernelGGL(k_quant_blocks<0>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax);
-  int64_t len = nb;
-  hipLaunchKernelGGL(k_tree_sum<float>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads), 0,
-                     s, absmax, len, buf0);
-  len = tree_partials(len);
-  double *cur = buf0, *nxt = buf1;
-  while (len > kTreeChunk) {
-    hipLaunchKernelGGL(k_tree_sum<double>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads),
-                       0, s, cur, len, nxt);
+    hipLaunchKernelGGL(k_quant_blocks<0>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax, sub);
+  const double *partials = sub;
+  if (len > kConstsMaxPartials) {   // n > 2^27: one more tree level (len <= 2^17 -> at most 64 sums)
+    hipLaunchKernelGGL(k_tree_sum<double>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads), 0, s,
+                       sub, len, level);
     len = tree_partials(len);
-    double *t = cur; cur = nxt; nxt = t;
+    partials = level;
   }
   const int64_t nb2 = (nb + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_quant_consts, dim3(grid_for(nb2, kThreads / 64, 4096)), dim3(kThreads), 0, s,
-                     absmax, nb, cur, len, code8, c2, mean);
+                     absmax, nb, partials, len, code8, c2, mean);
   return hipGetLastError();
 }
 
