@@ -85,6 +85,7 @@ constexpr bool q4_cells_separate() {
   return true;
 }
 static_assert(q4_cells_separate(), "4-bit thresholds too close to a coding cell edge");
+static_assert(kWgBlocks == kGroup, "a pass-1 workgroup writes whole groups of constants");
 
 // Cell table of table qtype into c[0 .. kCells): (bits of 16 tau or +inf, lo | hi << 16).
 __device__ __forceinline__ void build_cells(int qtype, uint2 *c) {
@@ -243,9 +244,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restric
   else
     quant_chunks<kIn, false>(W, n, qtype, packed, sCells + kCellUnit, sA);
   __syncthreads();
-  const int64_t nb = (n + kBlock - 1) / kBlock;
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * kWgBlocks + threadIdx.x;
-  if (b < nb) absmax[b] = sA[threadIdx.x];
+  // absmax holds whole groups of 256: blocks past nb (last workgroup) get 0.
+  absmax[static_cast<int64_t>(blockIdx.x) * kWgBlocks + threadIdx.x] = sA[threadIdx.x];
   if (threadIdx.x < 64) {
     const double r = tree256_wave0(sA);
     if (threadIdx.x == 0) subtree[blockIdx.x] = r;
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ i
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2.  Every workgroup first finishes the tree over the plen <= 8192
+// Pass 2.  Every wave first issues the read of its first group of
+// constants; every workgroup then finishes the tree over the plen <= 8192
 // subtree sums (thread t: sums 32 t .. 32 t + 31 by neighbour pairs in
 // registers, then the 256 thread sums as in tree256_wave0), then
 // mean = fl32(sum / nb).  One wave per group of 256 constants, 4 per lane:
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ i
 // +inf as a 256th sentinel).  c2 = 0 -> code 127.
 // ---------------------------------------------------------------------------
 constexpr int kConstsMaxPartials = 32 * kThreads;   // 8192
+static_assert(kThreads == 256, "one thread per 8-bit threshold-table entry");
 
 __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restrict__ absmax, int64_t nb,
                                                            const double *__restrict__ partials, int64_t plen,
@@ -308,11 +310,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
   __shared__ double s[kThreads];
   __shared__ float sMean;
   const int t = threadIdx.x;
-  for (int i = t; i < 256; i += kThreads) thr[i] = (i < 255) ? u2f(cT8Thresh[i]) : INFINITY;
+  const int lane = t & 63;
+  const int64_t nb2 = (nb + kGroup - 1) / kGroup;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  int64_t g = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (t >> 6);
+  // The wave's first group of constants, the subtree sums and the threshold
+  // table are all requested before any of them is used, so the three reads
+  // overlap.  absmax is padded to whole groups (zeros past nb).
+  f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (g < nb2) c = *reinterpret_cast<const f32x4_t *>(absmax + g * kGroup + lane * 4);
   {
     double v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = (32 * t + i < plen) ? partials[32 * t + i] : 0.0;
+    const float th = (t < 255) ? u2f(cT8Thresh[t]) : INFINITY;   // kThreads == 256 entries
+    thr[t] = th;
 #pragma unroll
     for (int w = 16; w >= 1; w >>= 1)
 #pragma unroll
@@ -328,15 +340,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
   const float mean = sMean;
   if (blockIdx.x == 0 && t == 0) mean_out[0] = mean;
 
-  const int lane = threadIdx.x & 63;
-  const int64_t nb2 = (nb + kGroup - 1) / kGroup;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6); g < nb2;
-       g += waves) {
+  for (; g < nb2; g += waves) {
     const int64_t idx = g * kGroup + lane * 4;
     float d[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = (idx + i < nb) ? (absmax[idx + i] - mean) : 0.0f;
+    for (int i = 0; i < 4; ++i) d[i] = (idx + i < nb) ? (c[i] - mean) : 0.0f;
+    if (g + waves < nb2) c = *reinterpret_cast<const f32x4_t *>(absmax + (g + waves) * kGroup + lane * 4);
     float m = fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3])));
     m = wave_max(m);
     uint32_t codes = 0;
@@ -449,18 +458,16 @@ size_t quantize_ws_bytes(int64_t n) {
   if (n < 1) return 0;
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t p = subtree_count(nb);
-  // absmax fp32 [nb] (padded to 256 B) | subtree sums fp64 [p] | next tree level fp64 [p / 2048]
-  const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
-  return a + static_cast<size_t>(p + tree_partials(p)) * 8;
+  // absmax fp32 [256 p] (whole groups; zeros past nb) | subtree sums fp64 [p] | next tree level fp64 [p / 2048]
+  return static_cast<size_t>(p) * kWgBlocks * 4 + static_cast<size_t>(p + tree_partials(p)) * 8;
 }
 
 hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uint8_t *packed, uint8_t *code8,
                            float *c2, float *mean, void *ws, hipStream_t s) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
-  const size_t a = ((static_cast<size_t>(nb) * 4 + 255) / 256) * 256;
-  float *absmax = static_cast<float *>(ws);
-  double *sub = reinterpret_cast<double *>(static_cast<char *>(ws) + a);
   int64_t len = subtree_count(nb);
+  float *absmax = static_cast<float *>(ws);
+  double *sub = reinterpret_cast<double *>(static_cast<char *>(ws) + static_cast<size_t>(len) * kWgBlocks * 4);
   double *level = sub + len;
 
   const dim3 g1(static_cast<unsigned>(len));

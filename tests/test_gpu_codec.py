@@ -109,6 +109,49 @@ def test_code_rule_near_every_threshold():
     _check(w.reshape(1, -1), "threshold_sweep")
 
 
+@pytest.mark.parametrize("qtype", ["nf4", "fp4", "int4"])
+def test_code_rule_near_thresholds_scaled(qtype):
+    # Block constants that are not powers of two (so no reciprocal of them is
+    # exact), from 1e5 down to below 2^-100, and elements w = fl32(x a) whose
+    # quotient x sits from 0 to 60000 fp32 steps either side of every
+    # decision threshold of the table: every code decided close to a
+    # threshold, inside and outside any approximation band, must match the
+    # oracle's rule on the correctly rounded quotient.
+    tau = nf4.midpoint_thresholds(nf4.q4_levels(qtype))
+    steps = [0, 1, 2, 3, 5, 8, 13, 40, 100, 300, 1000, 3000, 10000, 30000, 60000]
+    consts = [np.float32(c) for c in (1.7e5, 0.91, 0.0137, 3.7e-3, 2.3e-20, 1.3e-33, 3.1e-38)]
+    vals = []
+    for a in consts:
+        for t in np.unique(tau):
+            for k in steps:
+                for sgn in (1, -1):
+                    x = np.float32(t)
+                    xb = int(x.view(np.int32))
+                    key = (xb if x >= 0 else -(xb & 0x7FFFFFFF)) + sgn * k
+                    xk = np.array([key if key >= 0 else (-key) | 0x80000000], np.int64).astype(np.uint32).view(np.float32)[0]
+                    if abs(float(xk)) <= 1.0:
+                        vals.append((a, np.float32(xk * a)))
+    per_const = {}
+    for a, w in vals:
+        per_const.setdefault(float(a), []).append(w)
+    blocks = []
+    for i, (a, ws) in enumerate(sorted(per_const.items())):
+        ws = np.array(ws, np.float32)
+        for j in range(0, len(ws), 63):
+            blk = np.zeros(64, np.float32)
+            blk[0] = np.float32(a) if (i + j) % 2 == 0 else -np.float32(a)
+            part = ws[j:j + 63]
+            blk[1:1 + len(part)] = part
+            blocks.append(blk)
+    w = np.concatenate(blocks)[None, :-17]   # ragged end
+    print("codec case", qtype, "near thresholds scaled", w.shape, flush=True)
+    qw = q.NF4Weight.quantize(to_dev_f32(w), qtype)
+    torch.cuda.synchronize()
+    ref = nf4.quantize(w, qtype)
+    assert np.array_equal(qw.packed.cpu().numpy(), ref["packed"]), qtype + ": packed"
+    assert np.array_equal(qw.code8.cpu().numpy(), ref["code8"]), qtype + ": code8"
+
+
 def test_quantize_is_deterministic():
     rng = np.random.default_rng(8)
     w = to_dev_f32((rng.standard_normal((512, 2048)) * 0.02).astype(np.float32))
