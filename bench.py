@@ -303,14 +303,17 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True, patterns
     return out
 
 
-def quantize_bench(q, torch, workloads, cfg, dev, reps=10):
+def quantize_bench(q, torch, workloads, cfg, dev, reps=10, grouped=False):
     """Quantization (fp32 weights -> packed codes + double-quantized
     constants) of the 7 weights of a layer, over 4 weight sets (> the 256 MB
     Infinity Cache), through the C ABI with preallocated outputs and
-    workspaces, captured once in a HIP graph and replayed.  Algorithmic bytes
-    per parameter: 4 (fp32) read, 1/2 (codes) + 1/64 (constant codes) +
-    4/16384 (group scales) written."""
+    workspaces, captured once in a HIP graph and replayed: one
+    qlora_quantize_nf4 call per weight, or (grouped) one
+    qlora_quantize_nf4_group call per layer.  Algorithmic bytes per parameter:
+    4 (fp32) read, 1/2 (codes) + 1/64 (constant codes) + 4/16384 (group
+    scales) written."""
     import ctypes
+    from bit_nf4_quantized_absmax_amd._capi import NF4WeightStruct
     lib = q.lib()
     sets = []
     for si in range(4):
@@ -322,10 +325,22 @@ def quantize_bench(q, torch, workloads, cfg, dev, reps=10):
             nws = lib.qlora_quantize_workspace_bytes(rows * cols)
             ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
             items.append((W, w, w.struct(), ws, nws))
+        if grouped:
+            sts = (NF4WeightStruct * len(items))(*[it[2] for it in items])
+            ptrs = (ctypes.c_void_p * len(items))(*[it[0].data_ptr() for it in items])
+            gws_bytes = lib.qlora_quantize_group_workspace_bytes(len(items), sts)
+            gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev)
+            items = dict(items=items, sts=sts, ptrs=ptrs, ws=gws, nws=gws_bytes)
         sets.append(items)
 
     def run(stream):
         for items in sets:
+            if grouped:
+                rc = lib.qlora_quantize_nf4_group(len(items["items"]), items["ptrs"], 0, items["sts"],
+                                                  items["ws"].data_ptr(), items["nws"], stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("qlora_quantize_nf4_group failed: %d" % rc)
+                continue
             for W, _, st, ws, nws in items:
                 rc = lib.qlora_quantize_nf4(W.data_ptr(), ctypes.byref(st), ws.data_ptr(), nws, stream.cuda_stream)
                 if rc != 0:
@@ -356,7 +371,7 @@ def quantize_bench(q, torch, workloads, cfg, dev, reps=10):
     return dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
                 params=int(params), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
                 frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                launches_per_layer=2 * len(cfg.linears))
+                launches_per_layer=2 if grouped else 2 * len(cfg.linears))
 
 
 def q4_types_bench(q, torch, workloads, dev, reps=10):
@@ -538,13 +553,16 @@ def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3):
                 TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1), frac_bf16_peak=round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4))
 
 
-def dequantize_bench(q, torch, workloads, cfg, dev, reps=20):
+def dequantize_bench(q, torch, workloads, cfg, dev, reps=20, grouped=False):
     """Standalone dequantization (packed codes + constants -> bf16) of the 7
     weights of a layer, over 4 weight sets (> the 256 MB Infinity Cache),
-    captured once in a HIP graph with preallocated outputs and replayed.
-    Algorithmic bytes per parameter: 1/2 (codes) + 1/64 (constant codes) +
-    4/16384 (group scales) read, 2 (bf16) written."""
+    captured once in a HIP graph with preallocated outputs and replayed: one
+    qlora_dequantize_nf4 call per weight, or (grouped) one
+    qlora_dequantize_nf4_group call per layer.  Algorithmic bytes per
+    parameter: 1/2 (codes) + 1/64 (constant codes) + 4/16384 (group scales)
+    read, 2 (bf16) written."""
     import ctypes
+    from bit_nf4_quantized_absmax_amd._capi import NF4WeightStruct
     sets, outs = [], []
     for si in range(4):
         ws = []
@@ -556,8 +574,19 @@ def dequantize_bench(q, torch, workloads, cfg, dev, reps=20):
         outs.append([torch.empty(l.out_features, l.in_features, dtype=torch.bfloat16, device=dev) for l in cfg.linears])
     lib = q.lib()
 
+    groups = []
+    for si in range(4):
+        sts = sets[si][:-1]
+        groups.append(((NF4WeightStruct * len(sts))(*sts),
+                       (ctypes.c_void_p * len(sts))(*[o.data_ptr() for o in outs[si]])))
+
     def run(stream):
         for si in range(4):
+            if grouped:
+                rc = lib.qlora_dequantize_nf4_group(len(outs[si]), groups[si][0], groups[si][1], stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("qlora_dequantize_nf4_group failed: %d" % rc)
+                continue
             for st, o in zip(sets[si][:-1], outs[si]):
                 rc = lib.qlora_dequantize_nf4(ctypes.byref(st), o.data_ptr(), stream.cuda_stream)
                 if rc != 0:
@@ -587,7 +616,8 @@ def dequantize_bench(q, torch, workloads, cfg, dev, reps=20):
     torch.cuda.empty_cache()
     return dict(us_per_layer=round(us, 2), median_us=round(per[reps // 2], 2), min_us=round(per[0], 2),
                 params=int(params), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
-                frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), launches_per_layer=len(cfg.linears))
+                frac_hbm=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                launches_per_layer=1 if grouped else len(cfg.linears))
 
 
 def small_config_bench(q, torch, workloads, cfg, dev, reps=20):
@@ -645,8 +675,9 @@ def codec_cpu_baseline(workloads, cfg):
 
 
 def model_quantize_bench(q, torch, workloads, cfg, dev):
-    """Quantize every layer of a multi-layer config, weights drawn on the device
-    layer by layer (the draws are not timed)."""
+    """Quantize every layer of a multi-layer config, one grouped call
+    (qlora_quantize_nf4_group) per layer, weights drawn on the device layer by
+    layer (the draws are not timed)."""
     ms = 0.0
     params = 0
     stored = 0
@@ -655,7 +686,7 @@ def model_quantize_bench(q, torch, workloads, cfg, dev):
         Ws = [W for _, W in workloads.device_layer_weights(cfg, layer, dev)]
         torch.cuda.synchronize()
         e0.record()
-        ws = [q.NF4Weight.quantize(W) for W in Ws]
+        ws = q.quantize_group(Ws)
         e1.record()
         torch.cuda.synchronize()
         ms += e0.elapsed_time(e1)
@@ -706,7 +737,10 @@ def main():
         c1 = workloads.CONFIGS[1]
         print(json.dumps(dict(metric="NF4 codec GB/s (7B layer, 7 weights, 4 weight sets)", unit="GB/s",
                               data="synthetic", quantize=quantize_bench(q, torch, workloads, c1, dev),
-                              dequantize=dequantize_bench(q, torch, workloads, c1, dev))), flush=True)
+                              quantize_grouped=quantize_bench(q, torch, workloads, c1, dev, grouped=True),
+                              dequantize=dequantize_bench(q, torch, workloads, c1, dev),
+                              dequantize_grouped=dequantize_bench(q, torch, workloads, c1, dev, grouped=True))),
+              flush=True)
         return
     cfg = workloads.CONFIGS[1]
     scale = cfg.scale
@@ -764,8 +798,10 @@ def main():
         extras["small_m"] = small_m_bench(q, torch, workloads, workloads.CONFIGS[2], dev)
         log("quantize")
         extras["quantize"] = quantize_bench(q, torch, workloads, cfg, dev)
+        extras["quantize_grouped"] = quantize_bench(q, torch, workloads, cfg, dev, grouped=True)
         log("dequantize")
         extras["dequantize"] = dequantize_bench(q, torch, workloads, cfg, dev)
+        extras["dequantize_grouped"] = dequantize_bench(q, torch, workloads, cfg, dev, grouped=True)
         log("small parity configuration")
         extras["small_config"] = small_config_bench(q, torch, workloads, workloads.CONFIGS[0], dev)
         log("4-bit types")

@@ -21,6 +21,7 @@ STATIC_SCRATCH_BYTES = 16 << 20
 EXPORTED = (
     "qlora_status_string", "qlora_version", "qlora_nf4_sizes",
     "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_quantize_nf4_16", "qlora_dequantize_nf4",
+    "qlora_quantize_group_workspace_bytes", "qlora_quantize_nf4_group", "qlora_dequantize_nf4_group",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_bwd",
     "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in_workspace_bytes", "qlora_lora_grad_in",
     "qlora_nf4_matmul_dx",
@@ -76,6 +77,9 @@ _SIGS = {
     "qlora_quantize_nf4": (ctypes.c_int, [_vp, _wp, _vp, _sz, _vp]),
     "qlora_quantize_nf4_16": (ctypes.c_int, [_vp, ctypes.c_int32, _wp, _vp, _sz, _vp]),
     "qlora_dequantize_nf4": (ctypes.c_int, [_wp, _vp, _vp]),
+    "qlora_quantize_group_workspace_bytes": (_sz, [ctypes.c_int, _wp]),
+    "qlora_quantize_nf4_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_vp), _i32, _wp, _vp, _sz, _vp]),
+    "qlora_dequantize_nf4_group": (ctypes.c_int, [ctypes.c_int, _wp, ctypes.POINTER(_vp), _vp]),
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, ctypes.c_int]),
     "qlora_linear_fwd": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_fwd_noalloc": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _f32, _vp, _vp, _vp]),

@@ -179,6 +179,51 @@ int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *st
                                     static_cast<hipStream_t>(stream)));
 }
 
+constexpr int kCodecGroupMax = 8;
+
+size_t qlora_quantize_group_workspace_bytes(int count, const qlora_nf4_weight *out) {
+  if (count < 1 || count > kCodecGroupMax || !out) return 0;
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    if (out[i].rows < 1 || out[i].cols < 1 || out[i].rows > kMaxElems / out[i].cols) return 0;
+    total += round_up(quantize_ws_bytes(out[i].rows * out[i].cols), 256);
+  }
+  return total;
+}
+
+int qlora_quantize_nf4_group(int count, const void *const *W, int32_t in_type, const qlora_nf4_weight *out,
+                             void *ws, size_t ws_bytes, void *stream) {
+  if (count < 1 || count > kCodecGroupMax || !W || !out) return QLORA_ERR_INVALID_ARG;
+  if (in_type != 0 && in_type != QLORA_IN_BF16 && in_type != QLORA_IN_FP16) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    int st = check_weight(&out[i]);
+    if (st) return st;
+    if (!W[i] || !aligned(W[i], 16)) return QLORA_ERR_INVALID_ARG;
+  }
+  const size_t need = qlora_quantize_group_workspace_bytes(count, out);
+  if (!ws || !aligned(ws, 16) || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  QuantJob jobs[kCodecGroupMax];
+  char *p = static_cast<char *>(ws);
+  for (int i = 0; i < count; ++i) {
+    const int64_t n = out[i].rows * out[i].cols;
+    jobs[i] = QuantJob{W[i], n, out[i].qtype, out[i].packed, out[i].code8, out[i].c2, out[i].mean, p};
+    p += round_up(quantize_ws_bytes(n), 256);
+  }
+  return from_hip(launch_quantize_group(count, jobs, in_type, static_cast<hipStream_t>(stream)));
+}
+
+int qlora_dequantize_nf4_group(int count, const qlora_nf4_weight *w, uint16_t *const *out_bf16, void *stream) {
+  if (count < 1 || count > kCodecGroupMax || !w || !out_bf16) return QLORA_ERR_INVALID_ARG;
+  DequantJob jobs[kCodecGroupMax];
+  for (int i = 0; i < count; ++i) {
+    int st = check_weight(&w[i]);
+    if (st) return st;
+    if (!bf16_ok(out_bf16[i])) return QLORA_ERR_INVALID_ARG;
+    jobs[i] = DequantJob{w[i].packed, w[i].code8, w[i].c2, w[i].mean, w[i].rows * w[i].cols, w[i].qtype, out_bf16[i]};
+  }
+  return from_hip(launch_dequantize_group(count, jobs, static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int is_bwd) {
   if (M < 0 || N < 1 || K < 64 || K % 64 || N % 8 || r < 1 || r > 128) return 0;
   if (M > 0 && M > kMaxElems / std::max(N, K)) return 0;

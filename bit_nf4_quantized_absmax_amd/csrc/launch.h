@@ -10,13 +10,37 @@
 namespace qlora {
 
 // ---- codec ---------------------------------------------------------------
-// Workspace layout for quantize: absmax fp32 [nb] | tree partials fp64.
+// Workspace of one quantized weight: absmax fp32 in whole groups of 256 |
+// subtree sums fp64 | one further tree level fp64.
 size_t quantize_ws_bytes(int64_t n);
 // W: fp32 (in_type 0), bf16 (1) or fp16 (2) elements.
 hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uint8_t *packed, uint8_t *code8,
                            float *c2, float *mean, void *ws, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
                              const float *mean, int64_t n, int qtype, uint16_t *out, hipStream_t s);
+// Up to 8 weights per call: two launches for the whole group (quantize; one
+// more per member above 2^27 elements), one launch (dequantize).
+struct QuantJob {
+  const void *W;
+  int64_t n;
+  int qtype;
+  uint8_t *packed;
+  uint8_t *code8;
+  float *c2;
+  float *mean;
+  void *ws;   // quantize_ws_bytes(n) bytes, 16-byte aligned
+};
+hipError_t launch_quantize_group(int count, const QuantJob *jobs, int in_type, hipStream_t s);
+struct DequantJob {
+  const uint8_t *packed;
+  const uint8_t *code8;
+  const float *c2;
+  const float *mean;
+  int64_t n;
+  int qtype;
+  uint16_t *out;
+};
+hipError_t launch_dequantize_group(int count, const DequantJob *jobs, hipStream_t s);
 
 // ---- NF4 weight view passed to the matmul kernels ---------------------------
 struct NF4View {

@@ -64,6 +64,7 @@ constexpr int kCellUnit = 16;                            // cells per unit of x
 constexpr int kCells = 2 * kCellUnit + 1;                // x in [-1, 1]
 constexpr float kNearBand = 0x1p-15f;                    // |y - 16 tau| below this: exact recode
 constexpr float kTinyAbsmax = 0x1p-100f;                 // below this: exact recode
+constexpr int kCodecMaxGroup = 8;                        // weights per grouped launch
 
 // Compile-time check of the cell property for the three 4-bit tables: each
 // threshold at least 2^-4 from a cell edge (in 16 x units), ascending order.
@@ -149,10 +150,11 @@ __device__ __forceinline__ f32x4_t widen_chunk(const typename RawChunk<kIn>::typ
 // The 16 chunks of one thread, coded; kFull: the workgroup's range lies wholly below n.
 template <int kIn, bool kFull>
 __device__ __forceinline__ void quant_chunks(const void *__restrict__ W, int64_t n, int qtype,
-                                             uint8_t *__restrict__ packed, const uint2 *cells, float *sA) {
+                                             uint8_t *__restrict__ packed, int64_t wg, const uint2 *cells,
+                                             float *sA) {
   typedef typename RawChunk<kIn>::type raw_t;
   const int t = threadIdx.x;
-  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kWgElems;
+  const int64_t e0 = wg * kWgElems;
   raw_t r[kChunks];
   if (kFull) {
     const raw_t *src = reinterpret_cast<const raw_t *>(static_cast<const char *>(W) + e0 * (kIn == 0 ? 4 : 2)) + t;
@@ -230,25 +232,50 @@ __device__ __forceinline__ double tree256_wave0(const T *s) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// Grouped launches.  One launch serves up to kCodecMaxGroup weights (members):
+// member j owns the workgroups [wg_begin[j], wg_begin[j + 1]) of the grid and
+// each workgroup finds its member from blockIdx.x (uniform, scalar).  A
+// single weight is a group of one.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int codec_member(const int *wg_begin, int count) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kCodecMaxGroup; ++j)
+    i = (j < count && static_cast<int>(blockIdx.x) >= wg_begin[j]) ? j : i;
+  return i;
+}
+
+struct QuantBlocksArgs {
+  const void *W[kCodecMaxGroup];
+  int64_t n[kCodecMaxGroup];
+  uint8_t *packed[kCodecMaxGroup];
+  float *absmax[kCodecMaxGroup];
+  double *subtree[kCodecMaxGroup];
+  int qtype[kCodecMaxGroup];
+  int wg_begin[kCodecMaxGroup];
+  int count;
+};
+
 template <int kIn>
-__global__ __launch_bounds__(kThreads) void k_quant_blocks(const void *__restrict__ W, int64_t n, int qtype,
-                                                           uint8_t *__restrict__ packed,
-                                                           float *__restrict__ absmax,
-                                                           double *__restrict__ subtree) {
+__global__ __launch_bounds__(kThreads) void k_quant_blocks(const QuantBlocksArgs args) {
   __shared__ uint2 sCells[kCells];
   __shared__ float sA[kWgBlocks];
+  const int m = codec_member(args.wg_begin, args.count);
+  const int64_t wg = static_cast<int64_t>(blockIdx.x) - args.wg_begin[m];
+  const int64_t n = args.n[m];
+  const int qtype = args.qtype[m];
   build_cells(qtype, sCells);
-  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kWgElems;
-  if (e0 + kWgElems <= n)
-    quant_chunks<kIn, true>(W, n, qtype, packed, sCells + kCellUnit, sA);
+  if ((wg + 1) * kWgElems <= n)
+    quant_chunks<kIn, true>(args.W[m], n, qtype, args.packed[m], wg, sCells + kCellUnit, sA);
   else
-    quant_chunks<kIn, false>(W, n, qtype, packed, sCells + kCellUnit, sA);
+    quant_chunks<kIn, false>(args.W[m], n, qtype, args.packed[m], wg, sCells + kCellUnit, sA);
   __syncthreads();
   // absmax holds whole groups of 256: blocks past nb (last workgroup) get 0.
-  absmax[static_cast<int64_t>(blockIdx.x) * kWgBlocks + threadIdx.x] = sA[threadIdx.x];
+  args.absmax[m][wg * kWgBlocks + threadIdx.x] = sA[threadIdx.x];
   if (threadIdx.x < 64) {
     const double r = tree256_wave0(sA);
-    if (threadIdx.x == 0) subtree[blockIdx.x] = r;
+    if (threadIdx.x == 0) args.subtree[m][wg] = r;
   }
 }
 
@@ -301,19 +328,36 @@ __global__ __launch_bounds__(kThreads) void k_tree_sum(const Tin *__restrict__ i
 constexpr int kConstsMaxPartials = 32 * kThreads;   // 8192
 static_assert(kThreads == 256, "one thread per 8-bit threshold-table entry");
 
-__global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restrict__ absmax, int64_t nb,
-                                                           const double *__restrict__ partials, int64_t plen,
-                                                           uint8_t *__restrict__ code8,
-                                                           float *__restrict__ c2,
-                                                           float *__restrict__ mean_out) {
+struct QuantConstsArgs {
+  const float *absmax[kCodecMaxGroup];
+  int64_t nb[kCodecMaxGroup];
+  const double *partials[kCodecMaxGroup];
+  int64_t plen[kCodecMaxGroup];
+  uint8_t *code8[kCodecMaxGroup];
+  float *c2[kCodecMaxGroup];
+  float *mean[kCodecMaxGroup];
+  int wg_begin[kCodecMaxGroup];
+  int wgs[kCodecMaxGroup];
+  int count;
+};
+
+__global__ __launch_bounds__(kThreads) void k_quant_consts(const QuantConstsArgs args) {
   __shared__ float thr[256];
   __shared__ double s[kThreads];
   __shared__ float sMean;
+  const int mem = codec_member(args.wg_begin, args.count);
+  const float *__restrict__ absmax = args.absmax[mem];
+  const int64_t nb = args.nb[mem];
+  const double *__restrict__ partials = args.partials[mem];
+  const int64_t plen = args.plen[mem];
+  uint8_t *__restrict__ code8 = args.code8[mem];
+  float *__restrict__ c2 = args.c2[mem];
+  const int64_t wg = static_cast<int64_t>(blockIdx.x) - args.wg_begin[mem];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int64_t nb2 = (nb + kGroup - 1) / kGroup;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  int64_t g = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (t >> 6);
+  const int64_t waves = static_cast<int64_t>(args.wgs[mem]) * (kThreads / 64);
+  int64_t g = wg * (kThreads / 64) + (t >> 6);
   // The wave's first group of constants, the subtree sums and the threshold
   // table are all requested before any of them is used, so the three reads
   // overlap.  absmax is padded to whole groups (zeros past nb).
@@ -338,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
   }
   __syncthreads();
   const float mean = sMean;
-  if (blockIdx.x == 0 && t == 0) mean_out[0] = mean;
+  if (wg == 0 && t == 0) args.mean[mem][0] = mean;
 
   for (; g < nb2; g += waves) {
     const int64_t idx = g * kGroup + lane * 4;
@@ -384,23 +428,39 @@ __global__ __launch_bounds__(kThreads) void k_quant_consts(const float *__restri
 constexpr int kDqU = 8;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict__ packed,
-                                                      const uint8_t *__restrict__ code8,
-                                                      const float *__restrict__ c2,
-                                                      const float *__restrict__ mean_p, int64_t n, int qtype,
-                                                      uint16_t *__restrict__ out) {
+struct DequantArgs {
+  const uint8_t *packed[kCodecMaxGroup];
+  const uint8_t *code8[kCodecMaxGroup];
+  const float *c2[kCodecMaxGroup];
+  const float *mean[kCodecMaxGroup];
+  uint16_t *out[kCodecMaxGroup];
+  int64_t n[kCodecMaxGroup];
+  int qtype[kCodecMaxGroup];
+  int wg_begin[kCodecMaxGroup];
+  int wgs[kCodecMaxGroup];
+  int count;
+};
+
+__global__ __launch_bounds__(kThreads) void k_dequant(const DequantArgs args) {
   __shared__ float2 pairs[256];   // byte -> (level of its low nibble, level of its high nibble)
   __shared__ float t8[256];
+  const int mem = codec_member(args.wg_begin, args.count);
+  const uint8_t *__restrict__ packed = args.packed[mem];
+  const uint8_t *__restrict__ code8 = args.code8[mem];
+  const float *__restrict__ c2 = args.c2[mem];
+  uint16_t *__restrict__ out = args.out[mem];
+  const int64_t n = args.n[mem];
+  const int qtype = args.qtype[mem];
+  const int64_t wg = static_cast<int64_t>(blockIdx.x) - args.wg_begin[mem];
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     pairs[i] = make_float2(u2f(cQ4Level[16 * qtype + (i & 15)]), u2f(cQ4Level[16 * qtype + (i >> 4)]));
     t8[i] = u2f(cT8Level[i]);
   }
   __syncthreads();
-  const float mean = mean_p[0];
+  const float mean = args.mean[mem][0];
   const int64_t nchunks = (n + 7) / 8;
   const int64_t span = static_cast<int64_t>(kThreads) * kDqU;
-  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x; c0 < nchunks;
-       c0 += static_cast<int64_t>(gridDim.x) * span) {
+  for (int64_t c0 = wg * span + threadIdx.x; c0 < nchunks; c0 += static_cast<int64_t>(args.wgs[mem]) * span) {
     uint32_t p[kDqU], cc[kDqU];
     float sc[kDqU];
 #pragma unroll
@@ -462,39 +522,89 @@ size_t quantize_ws_bytes(int64_t n) {
   return static_cast<size_t>(p) * kWgBlocks * 4 + static_cast<size_t>(p + tree_partials(p)) * 8;
 }
 
+hipError_t launch_quantize_group(int count, const QuantJob *jobs, int in_type, hipStream_t s) {
+  if (count < 1 || count > kCodecMaxGroup) return hipErrorInvalidValue;
+  QuantBlocksArgs a1{};
+  QuantConstsArgs a2{};
+  a1.count = a2.count = count;
+  int64_t grid1 = 0, grid2 = 0;
+  for (int j = 0; j < count; ++j) {
+    const QuantJob &q = jobs[j];
+    const int64_t nb = (q.n + kBlock - 1) / kBlock;
+    const int64_t len = subtree_count(nb);
+    float *absmax = static_cast<float *>(q.ws);
+    double *sub = reinterpret_cast<double *>(static_cast<char *>(q.ws) + static_cast<size_t>(len) * kWgBlocks * 4);
+    a1.W[j] = q.W;
+    a1.n[j] = q.n;
+    a1.packed[j] = q.packed;
+    a1.absmax[j] = absmax;
+    a1.subtree[j] = sub;
+    a1.qtype[j] = q.qtype;
+    a1.wg_begin[j] = static_cast<int>(grid1);
+    grid1 += len;
+    a2.absmax[j] = absmax;
+    a2.nb[j] = nb;
+    a2.partials[j] = sub;
+    a2.plen[j] = len;
+    a2.code8[j] = q.code8;
+    a2.c2[j] = q.c2;
+    a2.mean[j] = q.mean;
+    a2.wg_begin[j] = static_cast<int>(grid2);
+    a2.wgs[j] = static_cast<int>(grid_for((nb + kGroup - 1) / kGroup, kThreads / 64, 4096));
+    grid2 += a2.wgs[j];
+  }
+  const dim3 g1(static_cast<unsigned>(grid1));
+  if (in_type == 1)
+    hipLaunchKernelGGL(k_quant_blocks<1>, g1, dim3(kThreads), 0, s, a1);
+  else if (in_type == 2)
+    hipLaunchKernelGGL(k_quant_blocks<2>, g1, dim3(kThreads), 0, s, a1);
+  else
+    hipLaunchKernelGGL(k_quant_blocks<0>, g1, dim3(kThreads), 0, s, a1);
+  for (int j = 0; j < count; ++j) {
+    if (a2.plen[j] > kConstsMaxPartials) {   // n > 2^27: one more tree level (len <= 2^17 -> at most 64 sums)
+      double *level = a1.subtree[j] + a2.plen[j];
+      hipLaunchKernelGGL(k_tree_sum<double>, dim3(static_cast<unsigned>(tree_partials(a2.plen[j]))), dim3(kThreads),
+                         0, s, a1.subtree[j], a2.plen[j], level);
+      a2.partials[j] = level;
+      a2.plen[j] = tree_partials(a2.plen[j]);
+    }
+  }
+  hipLaunchKernelGGL(k_quant_consts, dim3(static_cast<unsigned>(grid2)), dim3(kThreads), 0, s, a2);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void *W, int in_type, int64_t n, int qtype, uint8_t *packed, uint8_t *code8,
                            float *c2, float *mean, void *ws, hipStream_t s) {
-  const int64_t nb = (n + kBlock - 1) / kBlock;
-  int64_t len = subtree_count(nb);
-  float *absmax = static_cast<float *>(ws);
-  double *sub = reinterpret_cast<double *>(static_cast<char *>(ws) + static_cast<size_t>(len) * kWgBlocks * 4);
-  double *level = sub + len;
+  const QuantJob job{W, n, qtype, packed, code8, c2, mean, ws};
+  return launch_quantize_group(1, &job, in_type, s);
+}
 
-  const dim3 g1(static_cast<unsigned>(len));
-  if (in_type == 1)
-    hipLaunchKernelGGL(k_quant_blocks<1>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax, sub);
-  else if (in_type == 2)
-    hipLaunchKernelGGL(k_quant_blocks<2>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax, sub);
-  else
-    hipLaunchKernelGGL(k_quant_blocks<0>, g1, dim3(kThreads), 0, s, W, n, qtype, packed, absmax, sub);
-  const double *partials = sub;
-  if (len > kConstsMaxPartials) {   // n > 2^27: one more tree level (len <= 2^17 -> at most 64 sums)
-    hipLaunchKernelGGL(k_tree_sum<double>, dim3(static_cast<unsigned>(tree_partials(len))), dim3(kThreads), 0, s,
-                       sub, len, level);
-    len = tree_partials(len);
-    partials = level;
+hipError_t launch_dequantize_group(int count, const DequantJob *jobs, hipStream_t s) {
+  if (count < 1 || count > kCodecMaxGroup) return hipErrorInvalidValue;
+  DequantArgs a{};
+  a.count = count;
+  int64_t grid = 0;
+  for (int j = 0; j < count; ++j) {
+    const DequantJob &d = jobs[j];
+    a.packed[j] = d.packed;
+    a.code8[j] = d.code8;
+    a.c2[j] = d.c2;
+    a.mean[j] = d.mean;
+    a.out[j] = d.out;
+    a.n[j] = d.n;
+    a.qtype[j] = d.qtype;
+    a.wg_begin[j] = static_cast<int>(grid);
+    a.wgs[j] = static_cast<int>(grid_for((d.n + 7) / 8, kThreads * kDqU, 16384));
+    grid += a.wgs[j];
   }
-  const int64_t nb2 = (nb + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL(k_quant_consts, dim3(grid_for(nb2, kThreads / 64, 4096)), dim3(kThreads), 0, s,
-                     absmax, nb, partials, len, code8, c2, mean);
+  hipLaunchKernelGGL(k_dequant, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const uint8_t *packed, const uint8_t *code8, const float *c2,
                              const float *mean, int64_t n, int qtype, uint16_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(k_dequant, dim3(grid_for((n + 7) / 8, kThreads * kDqU, 16384)), dim3(kThreads), 0, s, packed,
-                     code8, c2, mean, n, qtype, out);
-  return hipGetLastError();
+  const DequantJob job{packed, code8, c2, mean, n, qtype, out};
+  return launch_dequantize_group(1, &job, s);
 }
 
 }  // namespace qlora

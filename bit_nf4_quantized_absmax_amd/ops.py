@@ -143,6 +143,48 @@ class NF4Weight:
         return sum(t.numel() * t.element_size() for t in (self.packed, self.code8, self.c2, self.mean))
 
 
+def quantize_group(Ws, qtypes=None):
+    """Quantize up to 8 device tensors [rows, cols] of one dtype (float32,
+    bfloat16 or float16) in one call (qlora_quantize_nf4_group: two launches
+    for the whole group).  qtypes: one 4-bit table name per tensor (default
+    all "nf4").  Returns one NF4Weight per tensor, bit-identical to
+    NF4Weight.quantize of each."""
+    Ws = list(Ws)
+    if not 1 <= len(Ws) <= 8:
+        raise ValueError("a group holds 1 to 8 weights")
+    qtypes = list(qtypes) if qtypes is not None else ["nf4"] * len(Ws)
+    if len(qtypes) != len(Ws):
+        raise ValueError("one qtype per weight")
+    dtype = Ws[0].dtype
+    in_type = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}.get(dtype)
+    if in_type is None:
+        raise ValueError("W must be float32, bfloat16 or float16")
+    for i, W in enumerate(Ws):
+        _need(W, dtype, "Ws[%d]" % i)
+        if W.dim() != 2:
+            raise ValueError("Ws[%d] must be 2-D [out_features, in_features]" % i)
+    outs = [NF4Weight.empty(W.shape[0], W.shape[1], W.device, qt) for W, qt in zip(Ws, qtypes)]
+    sts = (NF4WeightStruct * len(Ws))(*[w.struct() for w in outs])
+    ws_bytes = lib().qlora_quantize_group_workspace_bytes(len(Ws), sts)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Ws[0].device)
+    ptrs = (ctypes.c_void_p * len(Ws))(*[_ptr(W) for W in Ws])
+    check(lib().qlora_quantize_nf4_group(len(Ws), ptrs, in_type, sts, _ptr(ws), ws_bytes, _stream(Ws[0])),
+          "qlora_quantize_nf4_group")
+    return outs
+
+
+def dequantize_group(weights):
+    """bf16 copies of up to 8 NF4Weights in one launch (qlora_dequantize_nf4_group)."""
+    weights = list(weights)
+    if not 1 <= len(weights) <= 8:
+        raise ValueError("a group holds 1 to 8 weights")
+    outs = [torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device) for w in weights]
+    sts = (NF4WeightStruct * len(weights))(*[w.struct() for w in weights])
+    ptrs = (ctypes.c_void_p * len(weights))(*[_ptr(o) for o in outs])
+    check(lib().qlora_dequantize_nf4_group(len(weights), sts, ptrs, _stream(outs[0])), "qlora_dequantize_nf4_group")
+    return outs
+
+
 def _mat(t, name, dtype=torch.bfloat16):
     """A 2-D contiguous device tensor of `dtype`; returns its shape."""
     _need(t, dtype, name)

@@ -152,6 +152,35 @@ int qlora_quantize_nf4_16(const uint16_t *W, int32_t in_type, const qlora_nf4_we
  * to BFloat16 on the fly). */
 int qlora_dequantize_nf4(const qlora_nf4_weight *w, uint16_t *out_bf16, void *stream);
 
+/* Workspace bytes for qlora_quantize_nf4_group: the members'
+ * qlora_quantize_workspace_bytes, each rounded up to 256 bytes, summed.  0 if
+ * count < 1, count > 8, out is NULL or a member has rows or cols < 1 or
+ * rows * cols >= 2^31.  Host-only; reads only rows and cols. */
+size_t qlora_quantize_group_workspace_bytes(int count, const qlora_nf4_weight *out);
+
+/* Quantize up to 8 weights in one call, for example the seven projections of
+ * a layer as a checkpoint is loaded into 4 bits (creativeworksofknowledge.com,
+ * "QLoRA: Fine-Tune 70B on One GPU", Code).  Member i codes W[i] (fp32 when
+ * in_type = 0, else the 16-bit patterns of QLORA_IN_BF16 / QLORA_IN_FP16; one
+ * in_type for the whole group) into out[i] with out[i].qtype's table, under
+ * the rules of qlora_quantize_nf4.  Results are bit-identical to one
+ * qlora_quantize_nf4 / qlora_quantize_nf4_16 call per member; the group takes
+ * two launches in all (plus one per member above 2^27 elements) instead of two
+ * per member.  ws: device memory of qlora_quantize_group_workspace_bytes
+ * bytes, 16-byte aligned (each member's part starts on a 256-byte boundary).
+ * W[i]: 16-byte aligned.  Every member is validated before any launch
+ * (INVALID_ARG, UNSUPPORTED_SHAPE or WORKSPACE as for single calls; count
+ * outside 1..8 or a NULL array is INVALID_ARG). */
+int qlora_quantize_nf4_group(int count, const void *const *W, int32_t in_type, const qlora_nf4_weight *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Dequantize up to 8 weights in one launch: w[i] -> out_bf16[i] (rows x cols,
+ * 16-byte aligned), bit-identical to qlora_dequantize_nf4 per member.  Every
+ * member is validated before the launch; count outside 1..8 or a NULL array
+ * is INVALID_ARG.  Pages: automatone.win, "QLoRA paper explained", How it
+ * works (dequantize to BFloat16 on the fly). */
+int qlora_dequantize_nf4_group(int count, const qlora_nf4_weight *w, uint16_t *const *out_bf16, void *stream);
+
 /* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
  * (is_bwd = 1) at these sizes.  0 if the shape is unsupported, and 0 for a
  * forward pass at M = 0.  A forward pass at 1 <= M <= 64 with r % 8 == 0

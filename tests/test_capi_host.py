@@ -180,6 +180,42 @@ def test_validation_rejects_before_launch():
     assert L.qlora_dequantize_nf4(ctypes.byref(huge), P, None) == SHAPE
 
 
+def test_codec_group_validation_and_workspace():
+    L = q.lib()
+    P = ctypes.c_void_p(0x20000)
+    shapes = [(4096, 4096), (11008, 4096), (3, 65)]
+    ws = (_capi.NF4WeightStruct * 3)(*[_fake_weight(r, c, 0x100000 * (i + 1)) for i, (r, c) in enumerate(shapes)])
+    total = L.qlora_quantize_group_workspace_bytes(3, ws)
+    single = [L.qlora_quantize_workspace_bytes(r * c) for r, c in shapes]
+    assert total == sum((b + 255) // 256 * 256 for b in single)
+    assert L.qlora_quantize_group_workspace_bytes(0, ws) == 0
+    assert L.qlora_quantize_group_workspace_bytes(9, ws) == 0
+    assert L.qlora_quantize_group_workspace_bytes(3, None) == 0
+    bad = (_capi.NF4WeightStruct * 2)(_fake_weight(64, 64), _fake_weight(0, 64))
+    assert L.qlora_quantize_group_workspace_bytes(2, bad) == 0
+    Wp = (ctypes.c_void_p * 3)(0x20000, 0x30000, 0x40000)
+    assert L.qlora_quantize_nf4_group(0, Wp, 0, ws, P, total, None) == INVALID
+    assert L.qlora_quantize_nf4_group(9, Wp, 0, ws, P, total, None) == INVALID
+    assert L.qlora_quantize_nf4_group(3, None, 0, ws, P, total, None) == INVALID
+    assert L.qlora_quantize_nf4_group(3, Wp, 0, None, P, total, None) == INVALID
+    assert L.qlora_quantize_nf4_group(3, Wp, 3, ws, P, total, None) == INVALID          # in_type
+    assert L.qlora_quantize_nf4_group(2, Wp, 0, bad, P, 1 << 30, None) == INVALID       # member shape
+    Wmis = (ctypes.c_void_p * 3)(0x20000, 0x30004, 0x40000)
+    assert L.qlora_quantize_nf4_group(3, Wmis, 0, ws, P, total, None) == INVALID       # misaligned W
+    Wnull = (ctypes.c_void_p * 3)(0x20000, None, 0x40000)
+    assert L.qlora_quantize_nf4_group(3, Wnull, 1, ws, P, total, None) == INVALID
+    assert L.qlora_quantize_nf4_group(3, Wp, 0, ws, P, total - 1, None) == WS
+    assert L.qlora_quantize_nf4_group(3, Wp, 2, ws, None, total, None) == WS
+    outs = (ctypes.c_void_p * 3)(0x50000, 0x60000, 0x70000)
+    assert L.qlora_dequantize_nf4_group(0, ws, outs, None) == INVALID
+    assert L.qlora_dequantize_nf4_group(9, ws, outs, None) == INVALID
+    assert L.qlora_dequantize_nf4_group(3, None, outs, None) == INVALID
+    assert L.qlora_dequantize_nf4_group(3, ws, None, None) == INVALID
+    outs_bad = (ctypes.c_void_p * 3)(0x50000, 0x60008, 0x70000)
+    assert L.qlora_dequantize_nf4_group(3, ws, outs_bad, None) == INVALID
+    assert L.qlora_dequantize_nf4_group(2, bad, outs, None) == INVALID
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     W = torch.zeros(64, 64)

@@ -152,6 +152,47 @@ def test_code_rule_near_thresholds_scaled(qtype):
     assert np.array_equal(qw.code8.cpu().numpy(), ref["code8"]), qtype + ": code8"
 
 
+def _same_weight(a, b, name):
+    for f in ("packed", "code8", "c2", "mean"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), name + ": " + f
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_codec_group_matches_single_calls(dtype):
+    # One grouped quantize (two launches) and one grouped dequantize (one
+    # launch) over members of mixed shapes and 4-bit tables, ragged tails
+    # included: bit-identical to a single call per member.
+    rng = np.random.default_rng(77)
+    shapes = [(4096, 4096), (3, 65), (7, 1001), (64, 4096 + 64), (1, 64 * 257 + 3), (11008, 64)]
+    qtypes = ["nf4", "fp4", "int4", "nf4", "int4", "fp4"]
+    Ws = [torch.from_numpy((rng.standard_normal(sh) * 0.02).astype(np.float32)).to(DEV).to(dtype) for sh in shapes]
+    print("codec group case", dtype, shapes, flush=True)
+    grp = q.quantize_group(Ws, qtypes)
+    singles = [q.NF4Weight.quantize(W, qt) for W, qt in zip(Ws, qtypes)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(grp, singles)):
+        _same_weight(a, b, "member %d" % i)
+    deq = q.dequantize_group(grp)
+    for i, (d, w) in enumerate(zip(deq, singles)):
+        assert torch.equal(d.view(torch.int16), w.dequantize().view(torch.int16)), "dequant member %d" % i
+
+
+def test_codec_group_with_member_over_2_27():
+    # A member above 2^27 elements (8192 x 22016) adds its own tree launch
+    # inside the group; the small member beside it must be unaffected.
+    rng = np.random.default_rng(78)
+    big = (torch.randn(8192, 22016, device=DEV, generator=torch.Generator(DEV).manual_seed(5)) * 0.02)
+    small = torch.from_numpy((rng.standard_normal((5, 999)) * 0.02).astype(np.float32)).to(DEV)
+    print("codec group case big+small", flush=True)
+    grp = q.quantize_group([small, big], ["nf4", "nf4"])
+    s1 = q.NF4Weight.quantize(small)
+    s2 = q.NF4Weight.quantize(big)
+    torch.cuda.synchronize()
+    _same_weight(grp[0], s1, "small")
+    _same_weight(grp[1], s2, "big")
+    del big
+
+
 def test_quantize_is_deterministic():
     rng = np.random.default_rng(8)
     w = to_dev_f32((rng.standard_normal((512, 2048)) * 0.02).astype(np.float32))
