@@ -550,7 +550,9 @@ hipError_t launch_quantize_group(int count, const QuantJob *jobs, int in_type, h
     a2.c2[j] = q.c2;
     a2.mean[j] = q.mean;
     a2.wg_begin[j] = static_cast<int>(grid2);
-    a2.wgs[j] = static_cast<int>(grid_for((nb + kGroup - 1) / kGroup, kThreads / 64, 4096));
+    // At most 256 workgroups per member: each one repeats the tree over the
+    // member's subtree sums, so fewer, longer workgroups read less.
+    a2.wgs[j] = static_cast<int>(grid_for((nb + kGroup - 1) / kGroup, kThreads / 64, 256));
     grid2 += a2.wgs[j];
   }
   const dim3 g1(static_cast<unsigned>(grid1));
