@@ -26,6 +26,7 @@ EXPORTED = (
     "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_lora_grad_in_workspace_bytes", "qlora_lora_grad_in",
     "qlora_nf4_matmul_dx",
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
+    "qlora_lora_grads_group_workspace_bytes", "qlora_lora_grads_group",
     "qlora_linear_group_workspace_bytes", "qlora_linear_fwd_group",
     "qlora_lora_down_shared", "qlora_lora_dA_shared_workspace_bytes", "qlora_lora_dA_shared",
     "qlora_dropout_mask", "qlora_dropout_apply", "qlora_nf4_matmul_dx_dropout",
@@ -64,6 +65,21 @@ class LinearDescStruct(ctypes.Structure):
     ]
 
 
+class LoraGradsDescStruct(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p),
+        ("dY", ctypes.c_void_p),
+        ("G", ctypes.c_void_p),
+        ("T", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("r", ctypes.c_int32),
+        ("dA", ctypes.c_void_p),
+        ("dB", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
@@ -92,6 +108,8 @@ _SIGS = {
     "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
     "qlora_lora_grads_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_lora_grads_group_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(LoraGradsDescStruct)]),
+    "qlora_lora_grads_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LoraGradsDescStruct), _vp, _sz, _vp]),
     "qlora_linear_group_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(LinearDescStruct), _i64]),
     "qlora_linear_fwd_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearDescStruct), _i64, _vp, _sz, _vp]),
     "qlora_lora_down_shared": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.POINTER(_vp),

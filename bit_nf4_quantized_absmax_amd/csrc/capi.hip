@@ -338,18 +338,55 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grads_workspace_bytes(M, N, K, r))
     return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;   // nothing to reduce: dA and dB are left as they were
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int m = static_cast<int>(M);
-  if (dA) {
-    hipError_t e = launch_lora_grad_w(X, G, m, static_cast<int>(K), r, true, dA, ws, s);
-    if (e != hipSuccess) return QLORA_ERR_HIP;
+  GradWJob jobs[2];
+  int nj = 0;
+  if (dA) jobs[nj++] = GradWJob{X, G, m, static_cast<int>(K), r, true, dA, ws};
+  if (dB) jobs[nj++] = GradWJob{dY, T, m, static_cast<int>(N), r, false, dB, static_cast<char *>(ws) + pa};
+  if (nj == 0) return QLORA_OK;
+  return from_hip(launch_lora_grad_w_group(nj, jobs, static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_lora_grads_group_workspace_bytes(int count, const qlora_lora_grads_desc *d) {
+  if (count < 1 || count > 8 || !d) return 0;
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const size_t b = qlora_lora_grads_workspace_bytes(d[i].M, d[i].N, d[i].K, d[i].r);
+    if (b == 0) return 0;
+    total += b;
   }
-  if (dB) {
-    hipError_t e = launch_lora_grad_w(dY, T, m, static_cast<int>(N), r, false, dB,
-                                      static_cast<char *>(ws) + pa, s);
-    if (e != hipSuccess) return QLORA_ERR_HIP;
+  return total;
+}
+
+int qlora_lora_grads_group(int count, const qlora_lora_grads_desc *d, void *ws, size_t ws_bytes, void *stream) {
+  if (count < 1 || count > 8 || !d) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    const qlora_lora_grads_desc &x = d[i];
+    if (x.M < 0 || x.N < 1 || x.K < 1) return QLORA_ERR_INVALID_ARG;
+    if (x.r < 1 || x.r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if ((x.dA && (x.K < 8 || x.K % 8)) || (x.dB && (x.N < 8 || x.N % 8))) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if (x.M > 0 && x.M > kMaxElems / std::max(x.N, x.K)) return QLORA_ERR_UNSUPPORTED_SHAPE;
+    if (!bf16_opt(x.dA) || !bf16_opt(x.dB)) return QLORA_ERR_INVALID_ARG;
+    if (x.dA && (!rows_ok(x.X, x.M) || !rows_ok(x.G, x.M))) return QLORA_ERR_INVALID_ARG;
+    if (x.dB && (!rows_ok(x.dY, x.M) || !rows_ok(x.T, x.M))) return QLORA_ERR_INVALID_ARG;
   }
-  return QLORA_OK;
+  const size_t need = qlora_lora_grads_group_workspace_bytes(count, d);
+  if (!ws || !aligned(ws, 16) || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  GradWJob jobs[16];
+  int nj = 0;
+  char *p = static_cast<char *>(ws);
+  for (int i = 0; i < count; ++i) {
+    const qlora_lora_grads_desc &x = d[i];
+    const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(x.M), static_cast<int>(x.K), x.r), 256);
+    if (x.M > 0) {
+      const int m = static_cast<int>(x.M);
+      if (x.dA) jobs[nj++] = GradWJob{x.X, x.G, m, static_cast<int>(x.K), x.r, true, x.dA, p};
+      if (x.dB) jobs[nj++] = GradWJob{x.dY, x.T, m, static_cast<int>(x.N), x.r, false, x.dB, p + pa};
+    }
+    p += qlora_lora_grads_workspace_bytes(x.M, x.N, x.K, x.r);
+  }
+  if (nj == 0) return QLORA_OK;
+  return from_hip(launch_lora_grad_w_group(nj, jobs, static_cast<hipStream_t>(stream)));
 }
 
 int qlora_linear_fwd(const uint16_t *X, int64_t M, const qlora_nf4_weight *W, const uint16_t *A,
@@ -545,20 +582,17 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
     e = launch_matmul_dx(dY, m, v, G, A, r, dX, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
-  if (dA) {
-    e = launch_lora_grad_w(X, G, m, v.K, r, true, dA, pa, s);
+  const uint16_t *Tu = T;
+  if (dB && !Tu) {
+    e = launch_lora_down(X, m, v.K, A, r, scale, Tw, s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
+    Tu = Tw;
   }
-  if (dB) {
-    const uint16_t *Tu = T;
-    if (!Tu) {
-      e = launch_lora_down(X, m, v.K, A, r, scale, Tw, s);
-      if (e != hipSuccess) return QLORA_ERR_HIP;
-      Tu = Tw;
-    }
-    e = launch_lora_grad_w(dY, Tu, m, v.N, r, false, dB, pb, s);
-    if (e != hipSuccess) return QLORA_ERR_HIP;
-  }
+  GradWJob jobs[2];
+  int nj = 0;
+  if (dA) jobs[nj++] = GradWJob{X, G, m, v.K, r, true, dA, pa};
+  if (dB) jobs[nj++] = GradWJob{dY, Tu, m, v.N, r, false, dB, pb};
+  if (nj > 0 && launch_lora_grad_w_group(nj, jobs, s) != hipSuccess) return QLORA_ERR_HIP;
   return QLORA_OK;
 }
 
@@ -658,15 +692,16 @@ int qlora_linear_bwd_dropout(const uint16_t *dY, const uint16_t *X, const uint16
   if (dA || (dB && !T)) e = launch_dropout_apply(X, M * v.K, keep, Xd, s);
   if (e == hipSuccess && (dX || dA)) e = launch_lora_grad_in(dY, m, v.N, B, r, se, G, bt, s);
   if (e == hipSuccess && dX) e = launch_matmul_dx_drop(dY, m, v, G, A, r, keep, dX, s);
-  if (e == hipSuccess && dA) e = launch_lora_grad_w(Xd, G, m, v.K, r, true, dA, pa, s);
-  if (e == hipSuccess && dB) {
-    const uint16_t *Tu = T;
-    if (!Tu) {
-      e = launch_lora_down(Xd, m, v.K, A, r, se, Tw, s);
-      Tu = Tw;
-    }
-    if (e == hipSuccess) e = launch_lora_grad_w(dY, Tu, m, v.N, r, false, dB, pb, s);
+  const uint16_t *Tu = T;
+  if (e == hipSuccess && dB && !Tu) {
+    e = launch_lora_down(Xd, m, v.K, A, r, se, Tw, s);
+    Tu = Tw;
   }
+  GradWJob jobs[2];
+  int nj = 0;
+  if (dA) jobs[nj++] = GradWJob{Xd, G, m, v.K, r, true, dA, pa};
+  if (dB) jobs[nj++] = GradWJob{dY, Tu, m, v.N, r, false, dB, pb};
+  if (e == hipSuccess && nj > 0) e = launch_lora_grad_w_group(nj, jobs, s);
   return from_hip(e);
 }
 

@@ -171,6 +171,20 @@ hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t 
 // out = P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB);
 // D % 8 == 0; ws (lora_grad_ws_bytes): padded Q (r % 8 != 0) | split partials.
 size_t lora_grad_ws_bytes(int M, int D, int r);
+// Up to 16 such products (dA and dB of up to 8 linears) in one k_lora_tn
+// launch plus at most one partial-sum launch; each product as by
+// launch_lora_grad_w with its own workspace (lora_grad_ws_bytes).
+struct GradWJob {
+  const uint16_t *P;
+  const uint16_t *Q;
+  int M;
+  int D;
+  int r;
+  bool out_r_major;
+  uint16_t *out;
+  void *ws;
+};
+hipError_t launch_lora_grad_w_group(int count, const GradWJob *jobs, hipStream_t s);
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s);
 

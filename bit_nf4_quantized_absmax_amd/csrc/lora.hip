@@ -378,6 +378,7 @@ constexpr int kTnTile = kTnRows * 128;      // 4 KB
 constexpr int kTnStage = 2 * kTnTile;       // P then Q
 constexpr int kTnDma = 2 * kTnRows / 8;     // DMA instructions per stage
 constexpr int kTnRedPitch = 65;             // floats per row of a wave's 64 x 64 partial
+constexpr int kTnGroupMax = 16;             // products per grouped launch
 
 struct TnStage {
   bf16x8_t q[2][2], p[2][2];   // [sub-step][column block]
@@ -631,6 +632,75 @@ __global__ __launch_bounds__(256) void k_sum_partials(const float *__restrict__ 
   }
 }
 
+// Several k_lora_tn products in one launch (for example dA and dB of the
+// linears of a layer): problem i owns workgroups [wg0[i], wg0[i + 1]) and
+// decodes (d-tile, split, column chunk) from its local index; every tile is
+// computed exactly as by k_lora_tn, so results do not depend on the grouping.
+struct TnGroup {
+  const uint16_t *P[kTnGroupMax];
+  const uint16_t *Q[kTnGroupMax];
+  uint16_t *out[kTnGroupMax];
+  float *part[kTnGroupMax];
+  int64_t plane[kTnGroupMax];
+  int M[kTnGroupMax];
+  int D[kTnGroupMax];
+  int qcols[kTnGroupMax];
+  int r[kTnGroupMax];
+  int per[kTnGroupMax];
+  int pitch[kTnGroupMax];
+  int dt[kTnGroupMax];
+  int sp[kTnGroupMax];
+  int jmaj[kTnGroupMax];
+  int wg0[kTnGroupMax + 1];
+  int n;
+};
+
+__device__ __forceinline__ int tn_problem(const int *wg0, int n) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kTnGroupMax; ++j) i = (j < n && static_cast<int>(blockIdx.x) >= wg0[j]) ? j : i;
+  return i;
+}
+
+__global__ __launch_bounds__(kLoThreads) void k_lora_tn_group(const TnGroup g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLoWaves][kTnSlots][kTnStage];
+  const int i = tn_problem(g.wg0, g.n);
+  const int local = static_cast<int>(blockIdx.x) - g.wg0[i];
+  const int dt = local % g.dt[i];
+  const int sp = (local / g.dt[i]) % g.sp[i];
+  const int jc = local / (g.dt[i] * g.sp[i]);
+  lora_tn_tile(smem, g.P[i], g.M[i], g.D[i], g.Q[i], g.qcols[i], g.r[i], g.per[i], g.jmaj[i] != 0,
+               g.sp[i] == 1 ? g.out[i] : nullptr, g.part[i], g.plane[i], g.pitch[i], dt, sp, 64 * jc);
+}
+
+// The k_sum_partials of several products in one launch: problem i covers
+// elements [e0[i], e0[i + 1]) of the concatenated outputs.
+struct SumGroup {
+  const float *part[kTnGroupMax];
+  uint16_t *out[kTnGroupMax];
+  int64_t plane[kTnGroupMax];
+  int64_t e0[kTnGroupMax + 1];
+  int splits[kTnGroupMax];
+  int pitch[kTnGroupMax];
+  int ncol[kTnGroupMax];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void k_sum_partials_group(const SumGroup g) {
+  const int64_t total = g.e0[g.n];
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * 256) {
+    int i = 0;
+    for (int j = 1; j < g.n; ++j) i = idx >= g.e0[j] ? j : i;
+    const int64_t li = idx - g.e0[i];
+    const int row = static_cast<int>(li / g.ncol[i]), col = static_cast<int>(li % g.ncol[i]);
+    const float *p = g.part[i] + static_cast<int64_t>(row) * g.pitch[i] + col;
+    float sum = p[0];
+    for (int sp = 1; sp < g.splits[i]; ++sp) sum += p[sp * g.plane[i]];
+    g.out[i][li] = f32_to_bf16(sum);
+  }
+}
+
 // dst [rows, rq] = src [rows, r] with zero columns r .. rq - 1 (rq = r rounded
 // up to 8): 16-byte aligned rows for the DMA tiles.
 __global__ __launch_bounds__(256) void k_pad_cols(const uint16_t *__restrict__ src, int rows, int r, int rq,
@@ -777,35 +847,65 @@ hipError_t launch_lora_dA_shared(const uint16_t *X, int M, int K, int n, const u
   return hipSuccess;
 }
 
+hipError_t launch_lora_grad_w_group(int count, const GradWJob *jobs, hipStream_t s) {
+  if (count < 1 || count > kTnGroupMax) return hipErrorInvalidValue;
+  TnGroup g{};
+  SumGroup sg{};
+  g.n = count;
+  int64_t wg = 0, el = 0;
+  for (int i = 0; i < count; ++i) {
+    const GradWJob &jb = jobs[i];
+    const size_t pad = (jb.r & 7) ? align256(static_cast<size_t>(jb.M) * round8(jb.r) * 2) : 0;
+    int qcols = 0;
+    const uint16_t *Qp = padded(jb.Q, jb.M, jb.r, jb.ws, qcols, s);
+    const int sp = tn_splits(jb.M, jb.D);
+    const int jc = (jb.r + 63) / 64;
+    const int dt = (jb.D + 63) / 64;
+    const int nms = (jb.M + kTnRows - 1) / kTnRows;
+    // partial planes in the output orientation: [64 jc, dt * 64] or [dt * 64, 64 jc]
+    const int prow = jb.out_r_major ? 64 * jc : dt * 64;
+    const int pcol = jb.out_r_major ? dt * 64 : 64 * jc;
+    g.P[i] = jb.P;
+    g.Q[i] = Qp;
+    g.out[i] = jb.out;
+    g.part[i] = sp > 1 ? reinterpret_cast<float *>(static_cast<char *>(jb.ws) + pad) : nullptr;
+    g.plane[i] = static_cast<int64_t>(prow) * pcol;
+    g.M[i] = jb.M;
+    g.D[i] = jb.D;
+    g.qcols[i] = qcols;
+    g.r[i] = jb.r;
+    g.per[i] = (nms + sp - 1) / sp;
+    g.pitch[i] = pcol;
+    g.dt[i] = dt;
+    g.sp[i] = sp;
+    g.jmaj[i] = jb.out_r_major ? 1 : 0;
+    g.wg0[i] = static_cast<int>(wg);
+    wg += static_cast<int64_t>(dt) * sp * jc;
+    if (sp > 1) {
+      const int k = sg.n++;
+      sg.part[k] = g.part[i];
+      sg.out[k] = jb.out;
+      sg.plane[k] = g.plane[i];
+      sg.e0[k] = el;
+      sg.splits[k] = sp;
+      sg.pitch[k] = pcol;
+      sg.ncol[k] = jb.out_r_major ? jb.D : jb.r;
+      el += static_cast<int64_t>(jb.out_r_major ? jb.r : jb.D) * sg.ncol[k];
+    }
+  }
+  g.wg0[count] = static_cast<int>(wg);
+  sg.e0[sg.n] = el;
+  hipLaunchKernelGGL(k_lora_tn_group, dim3(static_cast<unsigned>(wg)), dim3(kLoThreads), 0, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sg.n == 0) return e;
+  hipLaunchKernelGGL(k_sum_partials_group, dim3(grid_for(el)), dim3(256), 0, s, sg);
+  return hipGetLastError();
+}
+
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s) {
-  const size_t pad = (r & 7) ? align256(static_cast<size_t>(M) * round8(r) * 2) : 0;
-  int qcols = 0;
-  const uint16_t *Qp = padded(Q, M, r, ws, qcols, s);
-  const int sp = tn_splits(M, D);
-  const int jc = (r + 63) / 64;
-  const int dt = (D + 63) / 64;
-  const int nms = (M + kTnRows - 1) / kTnRows;
-  const int per = (nms + sp - 1) / sp;
-  const dim3 grid(dt, sp, jc);
-  if (sp == 1) {
-    hipLaunchKernelGGL(k_lora_tn, grid, dim3(kLoThreads), 0, s, P, M, D, Qp, qcols, r, per, out_r_major, out,
-                       static_cast<float *>(nullptr), static_cast<int64_t>(0), 0);
-    return hipGetLastError();
-  }
-  // partial planes in the output orientation: [64 jc, dt * 64] or [dt * 64, 64 jc]
-  float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + pad);
-  const int prow = out_r_major ? 64 * jc : dt * 64;
-  const int pcol = out_r_major ? dt * 64 : 64 * jc;
-  const int64_t plane = static_cast<int64_t>(prow) * pcol;
-  hipLaunchKernelGGL(k_lora_tn, grid, dim3(kLoThreads), 0, s, P, M, D, Qp, qcols, r, per, out_r_major,
-                     static_cast<uint16_t *>(nullptr), part, plane, pcol);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nrow = out_r_major ? r : D, ncol = out_r_major ? D : r;
-  hipLaunchKernelGGL(k_sum_partials, dim3(grid_for(static_cast<int64_t>(nrow) * ncol)), dim3(256), 0, s, part, sp,
-                     plane, pcol, nrow, ncol, out);
-  return hipGetLastError();
+  const GradWJob job{P, Q, M, D, r, out_r_major, out, ws};
+  return launch_lora_grad_w_group(1, &job, s);
 }
 
 }  // namespace qlora

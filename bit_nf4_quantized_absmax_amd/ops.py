@@ -16,7 +16,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._capi import NF4WeightStruct, check, lib
+from ._capi import LoraGradsDescStruct, NF4WeightStruct, check, lib
 
 
 def _stream(t):
@@ -468,6 +468,38 @@ def lora_grads(X, dY, G, T, need_dA=True, need_dB=True, workspace=None, dA_out=N
     check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(G), _ptr(T), M, N, K, r, _ptr(dA), _ptr(dB), _ptr(ws),
                                  ws_bytes, _stream(X)), "qlora_lora_grads")
     return dA, dB
+
+
+def lora_grads_group(members, workspace=None):
+    """dA and dB of up to 8 linears in one contraction launch plus at most one
+    partial-sum launch (qlora_lora_grads_group).  members: sequence of dicts
+    with X, dY, G, T (as for lora_grads) and optional need_dA / need_dB,
+    dA_out / dB_out.  Returns [(dA, dB), ...], bit-identical to lora_grads of
+    each member."""
+    members = list(members)
+    if not 1 <= len(members) <= 8:
+        raise ValueError("a group holds 1 to 8 linears")
+    descs, outs = [], []
+    for i, mb in enumerate(members):
+        X, dY, G, T = mb["X"], mb["dY"], mb["G"], mb["T"]
+        M, K = _mat(X, "members[%d].X" % i)
+        N = _mat(dY, "members[%d].dY" % i)[1]
+        r = _mat(G, "members[%d].G" % i)[1]
+        _need(dY, torch.bfloat16, "members[%d].dY" % i, (M, N))
+        _need(G, torch.bfloat16, "members[%d].G" % i, (M, r))
+        _need(T, torch.bfloat16, "members[%d].T" % i, (M, r))
+        dev = X.device
+        dA = _out(mb.get("dA_out"), (r, K), dev, "members[%d].dA" % i) if mb.get("need_dA", True) else None
+        dB = _out(mb.get("dB_out"), (N, r), dev, "members[%d].dB" % i) if mb.get("need_dB", True) else None
+        descs.append(LoraGradsDescStruct(X.data_ptr(), dY.data_ptr(), G.data_ptr(), T.data_ptr(), M, N, K, r,
+                                         dA.data_ptr() if dA is not None else None,
+                                         dB.data_ptr() if dB is not None else None))
+        outs.append((dA, dB))
+    arr = (LoraGradsDescStruct * len(descs))(*descs)
+    X0 = members[0]["X"]
+    ws, ws_bytes = _workspace(workspace, lib().qlora_lora_grads_group_workspace_bytes(len(descs), arr), X0.device)
+    check(lib().qlora_lora_grads_group(len(descs), arr, _ptr(ws), ws_bytes, _stream(X0)), "qlora_lora_grads_group")
+    return outs
 
 
 # ---- autograd ----------------------------------------------------------------

@@ -347,12 +347,44 @@ size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t
  * T = scale X A^T as produced above (either output may be NULL).  The
  * contraction runs over M: when the d-tiles alone do not fill the GPU, M is
  * split and the fp32 split partials (in the workspace) are summed in split
- * order by a second pass (deterministic).  G and X are needed for dA (K % 8
+ * order by a second pass (deterministic).  dA and dB share one contraction
+ * launch and one partial-sum launch.  G and X are needed for dA (K % 8
  * == 0), dY and T for dB (N % 8 == 0).  M = 0 launches nothing and leaves dA
  * and dB as they were. */
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
                      const uint16_t *T, int64_t M, int64_t N, int64_t K, int32_t r,
                      uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes, void *stream);
+
+/* One linear's operands for qlora_lora_grads_group: the arguments of
+ * qlora_lora_grads, same meanings and rules (dA or dB may be NULL). */
+typedef struct {
+  const uint16_t *X;
+  const uint16_t *dY;
+  const uint16_t *G;
+  const uint16_t *T;
+  int64_t M;
+  int64_t N;
+  int64_t K;
+  int32_t r;
+  uint16_t *dA;
+  uint16_t *dB;
+} qlora_lora_grads_desc;
+
+/* Workspace bytes for qlora_lora_grads_group: the members'
+ * qlora_lora_grads_workspace_bytes summed (0 if count < 1, count > 8, d is
+ * NULL or a member's shape is unsupported). */
+size_t qlora_lora_grads_group_workspace_bytes(int count, const qlora_lora_grads_desc *d);
+
+/* dA and dB of up to 8 linears in one contraction launch plus at most one
+ * partial-sum launch, for example at the end of a layer's backward pass when
+ * every linear's G is known (adapters on every linear: creativeworksof
+ * knowledge.com, "QLoRA: Fine-Tune 70B on One GPU", Code).  Every member is
+ * computed exactly as by qlora_lora_grads (same tiles, splits and summation
+ * order): results are bit-identical.  ws: device memory of
+ * qlora_lora_grads_group_workspace_bytes bytes, 16-byte aligned; member i's
+ * part starts after the parts of members 0 .. i-1.  Every member is validated
+ * before any launch. */
+int qlora_lora_grads_group(int count, const qlora_lora_grads_desc *d, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- LoRA dropout on the adapter input -----------------------------------
  * The pages' adapters drop their input with probability p (creativeworksof

@@ -216,6 +216,39 @@ def test_codec_group_validation_and_workspace():
     assert L.qlora_dequantize_nf4_group(2, bad, outs, None) == INVALID
 
 
+def test_lora_grads_group_validation_and_workspace():
+    L = q.lib()
+    D = _capi.LoraGradsDescStruct
+    P = 0x20000
+    shapes = [(8192, 4096, 4096, 64), (8192, 11008, 4096, 64), (1000, 64, 128, 12)]
+    ds = (D * 3)(*[D(P, P, P, P, M, N, K, r, P, P) for M, N, K, r in shapes])
+    total = L.qlora_lora_grads_group_workspace_bytes(3, ds)
+    assert total == sum(L.qlora_lora_grads_workspace_bytes(M, N, K, r) for M, N, K, r in shapes)
+    assert L.qlora_lora_grads_group_workspace_bytes(0, ds) == 0
+    assert L.qlora_lora_grads_group_workspace_bytes(9, ds) == 0
+    assert L.qlora_lora_grads_group_workspace_bytes(3, None) == 0
+    wsp = ctypes.c_void_p(0x40000)
+    assert L.qlora_lora_grads_group(0, ds, wsp, total, None) == INVALID
+    assert L.qlora_lora_grads_group(9, ds, wsp, total, None) == INVALID
+    assert L.qlora_lora_grads_group(3, None, wsp, total, None) == INVALID
+    assert L.qlora_lora_grads_group(3, ds, wsp, total - 1, None) == WS
+    assert L.qlora_lora_grads_group(3, ds, None, total, None) == WS
+    bad_r = (D * 1)(D(P, P, P, P, 64, 64, 64, 129, P, P))
+    assert L.qlora_lora_grads_group(1, bad_r, wsp, 1 << 30, None) == SHAPE
+    bad_k = (D * 1)(D(P, P, P, P, 64, 64, 60, 8, P, None))      # dA needs K % 8 == 0
+    assert L.qlora_lora_grads_group(1, bad_k, wsp, 1 << 30, None) == SHAPE
+    bad_n = (D * 1)(D(P, P, P, P, 64, 60, 64, 8, None, P))      # dB needs N % 8 == 0
+    assert L.qlora_lora_grads_group(1, bad_n, wsp, 1 << 30, None) == SHAPE
+    neg = (D * 1)(D(P, P, P, P, -1, 64, 64, 8, P, P))
+    assert L.qlora_lora_grads_group(1, neg, wsp, 1 << 30, None) == INVALID
+    nox = (D * 2)(D(P, P, P, P, 64, 64, 64, 8, P, P), D(None, P, P, P, 64, 64, 64, 8, P, None))
+    assert L.qlora_lora_grads_group(2, nox, wsp, 1 << 30, None) == INVALID   # dA without X
+    mis = (D * 1)(D(P, P, P, P, 64, 64, 64, 8, 0x50008, P))
+    assert L.qlora_lora_grads_group(1, mis, wsp, 1 << 30, None) == INVALID   # misaligned dA
+    zero = (D * 1)(D(None, None, None, None, 0, 64, 64, 8, None, None))
+    assert L.qlora_lora_grads_group(1, zero, wsp, 1 << 30, None) == OK       # M = 0: nothing launched
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     W = torch.zeros(64, 64)
