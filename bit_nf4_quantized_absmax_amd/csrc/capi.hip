@@ -81,8 +81,9 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   w.t = bf16_bytes(M * r);
   w.g = bf16_bytes(M * r);
   w.bt = lora_grad_in_ws_bytes(static_cast<int>(N), r);
-  w.pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
-  w.pb = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r), 256);
+  const int gsp = lora_grad_pair_splits(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), r);
+  w.pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r, gsp), 256);
+  w.pb = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r, gsp), 256);
   w.total = w.t + w.g + w.bt + w.pa + w.pb;
   return w;
 }
@@ -320,8 +321,9 @@ int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W
 
 size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M < 0 || N < 1 || K < 1 || r < 1 || r > 128) return 0;
-  return round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256) +
-         round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r), 256);
+  const int sp = lora_grad_pair_splits(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), r);
+  return round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r, sp), 256) +
+         round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r, sp), 256);
 }
 
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, const uint16_t *T, int64_t M,
@@ -334,15 +336,17 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
   if (!bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
   if (dA && (!rows_ok(X, M) || !rows_ok(G, M))) return QLORA_ERR_INVALID_ARG;
   if (dB && (!rows_ok(dY, M) || !rows_ok(T, M))) return QLORA_ERR_INVALID_ARG;
-  const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r), 256);
+  const int psp = lora_grad_pair_splits(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), r);
+  const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r, psp), 256);
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grads_workspace_bytes(M, N, K, r))
     return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;   // nothing to reduce: dA and dB are left as they were
   const int m = static_cast<int>(M);
+  const int sp = psp;
   GradWJob jobs[2];
   int nj = 0;
-  if (dA) jobs[nj++] = GradWJob{X, G, m, static_cast<int>(K), r, true, dA, ws};
-  if (dB) jobs[nj++] = GradWJob{dY, T, m, static_cast<int>(N), r, false, dB, static_cast<char *>(ws) + pa};
+  if (dA) jobs[nj++] = GradWJob{X, G, m, static_cast<int>(K), r, true, dA, ws, sp};
+  if (dB) jobs[nj++] = GradWJob{dY, T, m, static_cast<int>(N), r, false, dB, static_cast<char *>(ws) + pa, sp};
   if (nj == 0) return QLORA_OK;
   return from_hip(launch_lora_grad_w_group(nj, jobs, static_cast<hipStream_t>(stream)));
 }
@@ -377,11 +381,12 @@ int qlora_lora_grads_group(int count, const qlora_lora_grads_desc *d, void *ws, 
   char *p = static_cast<char *>(ws);
   for (int i = 0; i < count; ++i) {
     const qlora_lora_grads_desc &x = d[i];
-    const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(x.M), static_cast<int>(x.K), x.r), 256);
+    const int sp = lora_grad_pair_splits(static_cast<int>(x.M), static_cast<int>(x.K), static_cast<int>(x.N), x.r);
+    const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(x.M), static_cast<int>(x.K), x.r, sp), 256);
     if (x.M > 0) {
       const int m = static_cast<int>(x.M);
-      if (x.dA) jobs[nj++] = GradWJob{x.X, x.G, m, static_cast<int>(x.K), x.r, true, x.dA, p};
-      if (x.dB) jobs[nj++] = GradWJob{x.dY, x.T, m, static_cast<int>(x.N), x.r, false, x.dB, p + pa};
+      if (x.dA) jobs[nj++] = GradWJob{x.X, x.G, m, static_cast<int>(x.K), x.r, true, x.dA, p, sp};
+      if (x.dB) jobs[nj++] = GradWJob{x.dY, x.T, m, static_cast<int>(x.N), x.r, false, x.dB, p + pa, sp};
     }
     p += qlora_lora_grads_workspace_bytes(x.M, x.N, x.K, x.r);
   }
@@ -588,10 +593,11 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
     if (e != hipSuccess) return QLORA_ERR_HIP;
     Tu = Tw;
   }
+  const int sp = lora_grad_pair_splits(m, v.K, v.N, r);
   GradWJob jobs[2];
   int nj = 0;
-  if (dA) jobs[nj++] = GradWJob{X, G, m, v.K, r, true, dA, pa};
-  if (dB) jobs[nj++] = GradWJob{dY, Tu, m, v.N, r, false, dB, pb};
+  if (dA) jobs[nj++] = GradWJob{X, G, m, v.K, r, true, dA, pa, sp};
+  if (dB) jobs[nj++] = GradWJob{dY, Tu, m, v.N, r, false, dB, pb, sp};
   if (nj > 0 && launch_lora_grad_w_group(nj, jobs, s) != hipSuccess) return QLORA_ERR_HIP;
   return QLORA_OK;
 }
@@ -697,10 +703,11 @@ int qlora_linear_bwd_dropout(const uint16_t *dY, const uint16_t *X, const uint16
     e = launch_lora_down(Xd, m, v.K, A, r, se, Tw, s);
     Tu = Tw;
   }
+  const int sp = lora_grad_pair_splits(m, v.K, v.N, r);
   GradWJob jobs[2];
   int nj = 0;
-  if (dA) jobs[nj++] = GradWJob{Xd, G, m, v.K, r, true, dA, pa};
-  if (dB) jobs[nj++] = GradWJob{dY, Tu, m, v.N, r, false, dB, pb};
+  if (dA) jobs[nj++] = GradWJob{Xd, G, m, v.K, r, true, dA, pa, sp};
+  if (dB) jobs[nj++] = GradWJob{dY, Tu, m, v.N, r, false, dB, pb, sp};
   if (e == hipSuccess && nj > 0) e = launch_lora_grad_w_group(nj, jobs, s);
   return from_hip(e);
 }

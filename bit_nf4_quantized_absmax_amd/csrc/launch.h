@@ -169,8 +169,9 @@ size_t lora_grad_in_ws_bytes(int N, int r);
 hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t *B, int r, float scale,
                                uint16_t *G, void *ws, hipStream_t s);
 // out = P^T Q over M, P [M, D], Q [M, r]; stored as [r, D] (dA) or [D, r] (dB);
-// D % 8 == 0; ws (lora_grad_ws_bytes): padded Q (r % 8 != 0) | split partials.
-size_t lora_grad_ws_bytes(int M, int D, int r);
+// D % 8 == 0; ws (lora_grad_ws_bytes): padded Q (r % 8 != 0) | split partials
+// for sp M-splits (sp <= 0: the product's own choice, as launch_lora_grad_w).
+size_t lora_grad_ws_bytes(int M, int D, int r, int sp);
 // Up to 16 such products (dA and dB of up to 8 linears) in one k_lora_tn
 // launch plus at most one partial-sum launch; each product as by
 // launch_lora_grad_w with its own workspace (lora_grad_ws_bytes).
@@ -183,8 +184,14 @@ struct GradWJob {
   bool out_r_major;
   uint16_t *out;
   void *ws;
+  int splits;   // M-splits of this product; 0: chosen for the product alone
 };
 hipError_t launch_lora_grad_w_group(int count, const GradWJob *jobs, hipStream_t s);
+// M-splits shared by one linear's dA [r, K] and dB [N, r] launched together:
+// chosen so that their tiles together fill the GPU in whole rounds.  Depends
+// on the shape only (not on which of dA and dB is requested), so each
+// output's bits do not depend on whether the other one is computed.
+int lora_grad_pair_splits(int M, int K, int N, int r);
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s);
 

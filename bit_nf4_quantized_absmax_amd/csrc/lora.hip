@@ -735,6 +735,25 @@ const uint16_t *padded(const uint16_t *src, int rows, int r, void *ws, int &cols
 // M-splits of k_lora_tn: enough workgroups to cover the 256 compute units in
 // whole rounds (one workgroup per CU: the LDS ring is 128 KB), at least 8
 // stages per split, a small penalty per extra split for the partial traffic.
+// Splits of one launch whose products together have `tiles` d-tile x column
+// chunk tiles (the same split for all of them).
+int tn_splits_tiles(int M, int tiles) {
+  const int nms = (M + kTnRows - 1) / kTnRows;
+  int best = 1;
+  double best_score = -1.0;
+  for (int sp = 1; sp <= 8; ++sp) {
+    if (sp > 1 && nms / sp < 8) break;
+    const int wg = tiles * sp;
+    const int rounds = (wg + 255) / 256;
+    const double score = static_cast<double>(wg) / (256.0 * rounds) - 0.03 * (sp - 1);
+    if (score > best_score + 1e-9) {
+      best = sp;
+      best_score = score;
+    }
+  }
+  return best;
+}
+
 int tn_splits(int M, int D) {
   const int dt = (D + 63) / 64;
   const int nms = (M + kTnRows - 1) / kTnRows;
@@ -776,9 +795,9 @@ hipError_t launch_lora_grad_in(const uint16_t *dY, int M, int N, const uint16_t 
 }
 
 // workspace: [padded Q (r % 8 != 0)] | [fp32 partials (more than one split)]
-size_t lora_grad_ws_bytes(int M, int D, int r) {
+size_t lora_grad_ws_bytes(int M, int D, int r, int sp) {
   const size_t pad = (r & 7) ? align256(static_cast<size_t>(M) * round8(r) * 2) : 0;
-  const int sp = tn_splits(M, D);
+  if (sp <= 0) sp = tn_splits(M, D);
   const int jc = (r + 63) / 64;
   const size_t part = sp > 1 ? align256(static_cast<size_t>(sp) * (64 * jc) * (((D + 63) / 64) * 64) * 4) : 0;
   return std::max<size_t>(pad + part, 256);
@@ -806,7 +825,7 @@ hipError_t launch_lora_down_shared(const uint16_t *X, int M, int K, int n, const
 // the layout of lora_grad_ws_bytes, one region after the other.
 size_t lora_dA_shared_ws_bytes(int M, int K, int n, const int *r) {
   size_t total = 0;
-  for (int i = 0; i < n; ++i) total += lora_grad_ws_bytes(M, K, r[i]);
+  for (int i = 0; i < n; ++i) total += lora_grad_ws_bytes(M, K, r[i], 0);
   return total;
 }
 
@@ -832,7 +851,7 @@ hipError_t launch_lora_dA_shared(const uint16_t *X, int M, int K, int n, const u
     sh.part[i] = sp > 1 ? reinterpret_cast<float *>(base + pad) : nullptr;
     sh.plane[i] = static_cast<int64_t>(64 * jc) * pcol;
     sh.y0[i + 1] = sh.y0[i] + jc;
-    base += lora_grad_ws_bytes(M, K, r[i]);
+    base += lora_grad_ws_bytes(M, K, r[i], 0);
   }
   const unsigned blocks = static_cast<unsigned>(dt) * static_cast<unsigned>(sp) * static_cast<unsigned>(sh.y0[n]);
   hipLaunchKernelGGL(k_lora_tn_shared, dim3(blocks), dim3(kLoThreads), 0, s, X, M, K, sp, per, true, pcol, sh);
@@ -858,7 +877,7 @@ hipError_t launch_lora_grad_w_group(int count, const GradWJob *jobs, hipStream_t
     const size_t pad = (jb.r & 7) ? align256(static_cast<size_t>(jb.M) * round8(jb.r) * 2) : 0;
     int qcols = 0;
     const uint16_t *Qp = padded(jb.Q, jb.M, jb.r, jb.ws, qcols, s);
-    const int sp = tn_splits(jb.M, jb.D);
+    const int sp = jb.splits > 0 ? jb.splits : tn_splits(jb.M, jb.D);
     const int jc = (jb.r + 63) / 64;
     const int dt = (jb.D + 63) / 64;
     const int nms = (jb.M + kTnRows - 1) / kTnRows;
@@ -902,9 +921,14 @@ hipError_t launch_lora_grad_w_group(int count, const GradWJob *jobs, hipStream_t
   return hipGetLastError();
 }
 
+int lora_grad_pair_splits(int M, int K, int N, int r) {
+  const int jc = (r + 63) / 64;
+  return tn_splits_tiles(M, jc * ((K + 63) / 64 + (N + 63) / 64));
+}
+
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s) {
-  const GradWJob job{P, Q, M, D, r, out_r_major, out, ws};
+  const GradWJob job{P, Q, M, D, r, out_r_major, out, ws, 0};
   return launch_lora_grad_w_group(1, &job, s);
 }
 
