@@ -81,9 +81,9 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   w.t = bf16_bytes(M * r);
   w.g = bf16_bytes(M * r);
   w.bt = lora_grad_in_ws_bytes(static_cast<int>(N), r);
-  const int gsp = lora_grad_pair_splits(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), r);
-  w.pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r, gsp), 256);
-  w.pb = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r, gsp), 256);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  w.pa = round_up(lora_grad_pair_ws_bytes(m, k, k, n, r), 256);
+  w.pb = round_up(lora_grad_pair_ws_bytes(m, n, k, n, r), 256);
   w.total = w.t + w.g + w.bt + w.pa + w.pb;
   return w;
 }
@@ -321,9 +321,8 @@ int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W
 
 size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M < 0 || N < 1 || K < 1 || r < 1 || r > 128) return 0;
-  const int sp = lora_grad_pair_splits(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), r);
-  return round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r, sp), 256) +
-         round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(N), r, sp), 256);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  return round_up(lora_grad_pair_ws_bytes(m, k, k, n, r), 256) + round_up(lora_grad_pair_ws_bytes(m, n, k, n, r), 256);
 }
 
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, const uint16_t *T, int64_t M,
@@ -336,13 +335,13 @@ int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G, c
   if (!bf16_opt(dA) || !bf16_opt(dB)) return QLORA_ERR_INVALID_ARG;
   if (dA && (!rows_ok(X, M) || !rows_ok(G, M))) return QLORA_ERR_INVALID_ARG;
   if (dB && (!rows_ok(dY, M) || !rows_ok(T, M))) return QLORA_ERR_INVALID_ARG;
-  const int psp = lora_grad_pair_splits(static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), r);
-  const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(M), static_cast<int>(K), r, psp), 256);
+  const size_t pa = round_up(
+      lora_grad_pair_ws_bytes(static_cast<int>(M), static_cast<int>(K), static_cast<int>(K), static_cast<int>(N), r), 256);
   if (!ws || !aligned(ws, 16) || ws_bytes < qlora_lora_grads_workspace_bytes(M, N, K, r))
     return QLORA_ERR_WORKSPACE;
   if (M == 0) return QLORA_OK;   // nothing to reduce: dA and dB are left as they were
   const int m = static_cast<int>(M);
-  const int sp = psp;
+  const int sp = lora_grad_splits(m, static_cast<int>(K), static_cast<int>(N), r, dA != nullptr, dB != nullptr);
   GradWJob jobs[2];
   int nj = 0;
   if (dA) jobs[nj++] = GradWJob{X, G, m, static_cast<int>(K), r, true, dA, ws, sp};
@@ -381,8 +380,9 @@ int qlora_lora_grads_group(int count, const qlora_lora_grads_desc *d, void *ws, 
   char *p = static_cast<char *>(ws);
   for (int i = 0; i < count; ++i) {
     const qlora_lora_grads_desc &x = d[i];
-    const int sp = lora_grad_pair_splits(static_cast<int>(x.M), static_cast<int>(x.K), static_cast<int>(x.N), x.r);
-    const size_t pa = round_up(lora_grad_ws_bytes(static_cast<int>(x.M), static_cast<int>(x.K), x.r, sp), 256);
+    const int xm = static_cast<int>(x.M), xk = static_cast<int>(x.K), xn = static_cast<int>(x.N);
+    const int sp = lora_grad_splits(xm, xk, xn, x.r, x.dA != nullptr, x.dB != nullptr);
+    const size_t pa = round_up(lora_grad_pair_ws_bytes(xm, xk, xk, xn, x.r), 256);
     if (x.M > 0) {
       const int m = static_cast<int>(x.M);
       if (x.dA) jobs[nj++] = GradWJob{x.X, x.G, m, static_cast<int>(x.K), x.r, true, x.dA, p, sp};
@@ -593,7 +593,7 @@ int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, i
     if (e != hipSuccess) return QLORA_ERR_HIP;
     Tu = Tw;
   }
-  const int sp = lora_grad_pair_splits(m, v.K, v.N, r);
+  const int sp = lora_grad_splits(m, v.K, v.N, r, dA != nullptr, dB != nullptr);
   GradWJob jobs[2];
   int nj = 0;
   if (dA) jobs[nj++] = GradWJob{X, G, m, v.K, r, true, dA, pa, sp};
@@ -703,7 +703,7 @@ int qlora_linear_bwd_dropout(const uint16_t *dY, const uint16_t *X, const uint16
     e = launch_lora_down(Xd, m, v.K, A, r, se, Tw, s);
     Tu = Tw;
   }
-  const int sp = lora_grad_pair_splits(m, v.K, v.N, r);
+  const int sp = lora_grad_splits(m, v.K, v.N, r, dA != nullptr, dB != nullptr);
   GradWJob jobs[2];
   int nj = 0;
   if (dA) jobs[nj++] = GradWJob{Xd, G, m, v.K, r, true, dA, pa, sp};

@@ -188,10 +188,14 @@ struct GradWJob {
 };
 hipError_t launch_lora_grad_w_group(int count, const GradWJob *jobs, hipStream_t s);
 // M-splits shared by one linear's dA [r, K] and dB [N, r] launched together:
-// chosen so that their tiles together fill the GPU in whole rounds.  Depends
-// on the shape only (not on which of dA and dB is requested), so each
-// output's bits do not depend on whether the other one is computed.
+// chosen so that their tiles together fill the GPU in whole rounds.
 int lora_grad_pair_splits(int M, int K, int N, int r);
+// Splits used for one linear: the shared count when both dA and dB are
+// computed, else the single product's own (tn_splits, as the shared-input dA).
+int lora_grad_splits(int M, int K, int N, int r, bool dA, bool dB);
+// Workspace of one of the pair's products (D = K for dA, N for dB), large
+// enough for either split choice.
+size_t lora_grad_pair_ws_bytes(int M, int D, int K, int N, int r);
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s);
 

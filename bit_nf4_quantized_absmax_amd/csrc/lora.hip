@@ -926,6 +926,15 @@ int lora_grad_pair_splits(int M, int K, int N, int r) {
   return tn_splits_tiles(M, jc * ((K + 63) / 64 + (N + 63) / 64));
 }
 
+int lora_grad_splits(int M, int K, int N, int r, bool dA, bool dB) {
+  if (dA && dB) return lora_grad_pair_splits(M, K, N, r);
+  return dA ? tn_splits(M, K) : tn_splits(M, N);
+}
+
+size_t lora_grad_pair_ws_bytes(int M, int D, int K, int N, int r) {
+  return lora_grad_ws_bytes(M, D, r, std::max(tn_splits(M, D), lora_grad_pair_splits(M, K, N, r)));
+}
+
 hipError_t launch_lora_grad_w(const uint16_t *P, const uint16_t *Q, int M, int D, int r, bool out_r_major,
                               uint16_t *out, void *ws, hipStream_t s) {
   const GradWJob job{P, Q, M, D, r, out_r_major, out, ws, 0};

@@ -346,9 +346,12 @@ size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t
 /* dA [r, K] = G^T X and/or dB [N, r] = dY^T T, with G = scale dY B and
  * T = scale X A^T as produced above (either output may be NULL).  The
  * contraction runs over M.  dA and dB share one contraction launch; when
- * their tiles together do not fill the GPU, M is split (one split count for
- * both, chosen from M, N, K and r only) and the fp32 split partials (in the
- * workspace) are summed in split order by one more launch (deterministic).  G and X are needed for dA (K % 8
+ * their tiles do not fill the GPU, M is split and the fp32 split partials (in
+ * the workspace) are summed in split order by one more launch
+ * (deterministic).  The split count comes from the shape: one count for both
+ * when both are computed (their tiles together fill the GPU in whole
+ * rounds), else the single product's own, the one qlora_lora_dA_shared uses;
+ * so dA's rounding can differ by whether dB is computed in the same call.  G and X are needed for dA (K % 8
  * == 0), dY and T for dB (N % 8 == 0).  M = 0 launches nothing and leaves dA
  * and dB as they were. */
 int qlora_lora_grads(const uint16_t *X, const uint16_t *dY, const uint16_t *G,
