@@ -148,23 +148,44 @@ class Layer:
         self.dx_mm_flops = 2.0 * M * N * K + 2.0 * M * r * K
 
 
+# Forward groups of a LLaMA layer: the products computed together (q, k and v
+# from one normalized input; gate and up from the next); each group's forward
+# matmuls run as one launch over their concatenated tiles.
+FWD_GROUPS = (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",))
+
+
+def fwd_groups(layers):
+    by = {L.name: L for L in layers}
+    if sorted(by) == sorted(n for g in FWD_GROUPS for n in g):
+        return [[by[n] for n in g] for g in FWD_GROUPS]
+    return [[L] for L in layers]
+
+
 def run_step(q, torch, layers, scale, events=None):
-    for L in layers:
-        q.lora_down(L.X, L.A, scale, out=L.T)
+    """One fwd + bwd of every linear: per forward group the LoRA-down of each
+    member, the group's fused forward matmuls (one launch), then per member
+    G, the fused dX matmul and dA / dB."""
+    for grp in fwd_groups(layers):
+        for L in grp:
+            q.lora_down(L.X, L.A, scale, out=L.T)
         if events is not None:
-            events["fwd"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), L))
+            events["fwd"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), grp))
             events["fwd"][-1][0].record()
-        q.nf4_matmul_fwd(L.X, L.w, L.T, L.B, out=L.Y)
+        if len(grp) > 1:
+            q.nf4_matmul_fwd_group([dict(X=L.X, w=L.w, T=L.T, B=L.B, out=L.Y) for L in grp])
+        else:
+            q.nf4_matmul_fwd(grp[0].X, grp[0].w, grp[0].T, grp[0].B, out=grp[0].Y)
         if events is not None:
             events["fwd"][-1][1].record()
-        q.lora_grad_in(L.dY, L.B, scale, out=L.G, workspace=L.gws)
-        if events is not None:
-            events["dx"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), L))
-            events["dx"][-1][0].record()
-        q.nf4_matmul_dx(L.dY, L.w, L.G, L.A, out=L.dX)
-        if events is not None:
-            events["dx"][-1][1].record()
-        q.lora_grads(L.X, L.dY, L.G, L.T, workspace=L.ws)
+        for L in grp:
+            q.lora_grad_in(L.dY, L.B, scale, out=L.G, workspace=L.gws)
+            if events is not None:
+                events["dx"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), [L]))
+                events["dx"][-1][0].record()
+            q.nf4_matmul_dx(L.dY, L.w, L.G, L.A, out=L.dX)
+            if events is not None:
+                events["dx"][-1][1].record()
+            q.lora_grads(L.X, L.dY, L.G, L.T, workspace=L.ws)
 
 
 def cpu_baseline(cfg, tokens):
@@ -772,7 +793,7 @@ def main():
     kern = {}
     for key, evs in events.items():
         tot_ms = sum(a.elapsed_time(b) for a, b, _ in evs)
-        flops = sum((L.fwd_mm_flops if key == "fwd" else L.dx_mm_flops) for _, _, L in evs)
+        flops = sum((L.fwd_mm_flops if key == "fwd" else L.dx_mm_flops) for _, _, grp in evs for L in grp)
         kern[key] = dict(launches=len(evs), avg_us=tot_ms * 1e3 / len(evs),
                          flops_per_launch=flops / len(evs), total_ms=tot_ms)
     dom_key = max(kern, key=lambda k: kern[k]["total_ms"])

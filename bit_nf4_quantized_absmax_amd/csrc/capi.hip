@@ -552,11 +552,51 @@ int qlora_linear_fwd_group(int count, const qlora_linear_desc *d, int64_t M, voi
                          : launch_lora_down(d[i].X, m, K, A[0], r[0], sc[0], Ts[0], s);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
+  // The fused matmuls: members in the decode regime one call each, the others
+  // in launches of up to 4 (one tile space per launch, so a launch's last
+  // partial round of tiles is shared by its members).
+  MatmulJob jobs[4];
+  int nj = 0;
   for (int i = 0; i < count; ++i) {
-    hipError_t e = launch_matmul_fwd(d[i].X, m, view_of(d[i].W), T[i], d[i].B, d[i].r, d[i].Y, s);
-    if (e != hipSuccess) return QLORA_ERR_HIP;
+    const qlora_linear_desc &x = d[i];
+    if (small_m_ok(M, x.r)) {
+      if (launch_matmul_fwd(x.X, m, view_of(x.W), T[i], x.B, x.r, x.Y, s) != hipSuccess) return QLORA_ERR_HIP;
+      continue;
+    }
+    jobs[nj++] = MatmulJob{x.X, T[i], x.B, nullptr, x.Y, view_of(x.W), m, x.r};
+    if (nj == 4) {
+      if (launch_matmul_fwd_group(nj, jobs, s) != hipSuccess) return QLORA_ERR_HIP;
+      nj = 0;
+    }
   }
+  if (nj > 0 && launch_matmul_fwd_group(nj, jobs, s) != hipSuccess) return QLORA_ERR_HIP;
   return QLORA_OK;
+}
+
+int qlora_nf4_matmul_fwd_group(int count, const qlora_matmul_fwd_desc *d, void *stream) {
+  if (count < 1 || count > 4 || !d) return QLORA_ERR_INVALID_ARG;
+  const int64_t M = d[0].M;
+  for (int i = 0; i < count; ++i) {
+    if (d[i].M != M) return QLORA_ERR_INVALID_ARG;
+    int st = check_linear_shape(M, d[i].W, d[i].r, 1.0f);
+    if (st) return st;
+    if (!rows_ok(d[i].X, M) || !rows_ok(d[i].T, M) || !bf16_ok(d[i].B) || !rows_ok(d[i].Y, M))
+      return QLORA_ERR_INVALID_ARG;
+  }
+  if (M == 0) return QLORA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int m = static_cast<int>(M);
+  MatmulJob jobs[4];
+  int nj = 0;
+  for (int i = 0; i < count; ++i) {
+    if (small_m_ok(M, d[i].r)) {   // the decode regime takes its own route, one call each
+      if (launch_matmul_fwd(d[i].X, m, view_of(d[i].W), d[i].T, d[i].B, d[i].r, d[i].Y, s) != hipSuccess)
+        return QLORA_ERR_HIP;
+      continue;
+    }
+    jobs[nj++] = MatmulJob{d[i].X, d[i].T, d[i].B, nullptr, d[i].Y, view_of(d[i].W), m, d[i].r};
+  }
+  return nj > 0 ? from_hip(launch_matmul_fwd_group(nj, jobs, s)) : QLORA_OK;
 }
 
 int qlora_linear_bwd(const uint16_t *dY, const uint16_t *X, const uint16_t *T, int64_t M,

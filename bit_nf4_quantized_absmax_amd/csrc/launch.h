@@ -54,6 +54,21 @@ struct NF4View {
 };
 
 // ---- large-M matmuls (T and G already carry the LoRA scale) ---------------------
+// One product of a grouped launch: left operand L [M, contraction], the LoRA
+// pair (Ln = T or G, Rn = B or A), mask (dropout dX only) and output.
+struct MatmulJob {
+  const uint16_t *L;
+  const uint16_t *Ln;
+  const uint16_t *Rn;
+  const uint32_t *keep;
+  uint16_t *out;
+  NF4View w;
+  int M;
+  int r;
+};
+// Up to 4 forward products (M >= 65 each) in one launch over their
+// concatenated tile grids; each output as launch_matmul_fwd computes it.
+hipError_t launch_matmul_fwd_group(int count, const MatmulJob *jobs, hipStream_t s);
 // Y [M, N] = X deq(W)^T + T B^T
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s);

@@ -56,6 +56,23 @@ namespace qlora {
 __constant__ uint32_t cMMQ4Level[3 * 16] = {QLORA_Q4_LEVEL_BITS};
 __constant__ uint32_t cMMT8Level[256] = {QLORA_T8_LEVEL_BITS};
 
+// Operands of up to kMmGroupMax products in one launch (a single call is a
+// group of one): left operand, LoRA pair, dropout mask and output per member.
+constexpr int kMmGroupMax = 4;
+struct MatmulArgs {
+  const uint16_t *L[kMmGroupMax];
+  const uint16_t *Ln[kMmGroupMax];
+  const uint16_t *Rn[kMmGroupMax];
+  const uint32_t *keep[kMmGroupMax];
+  uint16_t *out[kMmGroupMax];
+  NF4View w[kMmGroupMax];
+  int M[kMmGroupMax];
+  int r[kMmGroupMax];
+  int tcols[kMmGroupMax];
+  int t0[kMmGroupMax + 1];
+  int n;
+};
+
 namespace {
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -287,15 +304,21 @@ __device__ __forceinline__ void load_a_tile(uint8_t *stage, const uint16_t *A, i
   }
 }
 
-// Tile index -> (tile_row, tile_col).  Hardware spreads consecutive workgroups
-// over the 8 XCDs; remap so consecutive logical tiles (which share rows of the
-// left operand) run on the same XCD.
-__device__ __forceinline__ void tile_coords(int tiles_cols, int &tr, int &tc) {
+// Workgroup -> (member, tile_row, tile_col).  Hardware spreads consecutive
+// workgroups over the 8 XCDs; remap so consecutive logical tiles (which share
+// rows of the left operand) run on the same XCD.  Member j of a grouped launch
+// owns logical tiles [t0[j], t0[j + 1]), row-major over its own tile grid.
+__device__ __forceinline__ int tile_coords(const MatmulArgs &a, int &tr, int &tc) {
   int lid = blockIdx.x;
   const int nt = gridDim.x;
   if ((nt & 7) == 0) lid = (blockIdx.x & 7) * (nt >> 3) + (blockIdx.x >> 3);
-  tr = lid / tiles_cols;
-  tc = lid % tiles_cols;
+  int m = 0;
+#pragma unroll
+  for (int j = 1; j < kMmGroupMax; ++j) m = (j < a.n && lid >= a.t0[j]) ? j : m;
+  const int local = lid - a.t0[m];
+  tr = local / a.tcols[m];
+  tc = local % a.tcols[m];
+  return m;
 }
 
 }  // namespace
@@ -307,11 +330,7 @@ __device__ __forceinline__ void tile_coords(int tiles_cols, int &tr, int &tc) {
 // [m][k / 32]); the LoRA steps then run first, the mask zeroes their dropped
 // elements in the accumulators, and the base contraction follows.
 template <bool kDx, bool kDrop>
-__global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restrict__ L, int M, NF4View w,
-                                                       const uint16_t *__restrict__ Ln,
-                                                       const uint16_t *__restrict__ Rn, int r,
-                                                       const uint32_t *__restrict__ keep,
-                                                       uint16_t *__restrict__ out) {
+__global__ __launch_bounds__(kThreadsMM) void k_matmul(const MatmulArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t sX0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sX1[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sW0[kStageBytes];
@@ -319,11 +338,18 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
   __shared__ __attribute__((aligned(64))) float sNf4[16];
   __shared__ float sT8[256];
 
+  int tr, tc;
+  const int mem = tile_coords(args, tr, tc);
+  const uint16_t *__restrict__ L = args.L[mem];
+  const uint16_t *__restrict__ Ln = args.Ln[mem];
+  const uint16_t *__restrict__ Rn = args.Rn[mem];
+  const uint32_t *__restrict__ keep = args.keep[mem];
+  uint16_t *__restrict__ out = args.out[mem];
+  const NF4View w = args.w[mem];
+  const int M = args.M[mem], r = args.r[mem];
   const int K = w.K, N = w.N;
   const int ncols = kDx ? K : N;           // output columns
   const int Kc = kDx ? N : K;              // contraction length (multiple of 8; of 64 for the forward)
-  int tr, tc;
-  tile_coords((ncols + kBN - 1) / kBN, tr, tc);
   const int m0 = tr * kBM, c0 = tc * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -525,28 +551,55 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const uint16_t *__restric
 }
 
 // ---------------------------------------------------------------------------
+// A group of products of one kind (forward or dX, with or without the mask):
+// one launch over the concatenated tile grids.
+template <bool kDx, bool kDrop>
+static hipError_t launch_mm_group(int count, const MatmulJob *jobs, hipStream_t s) {
+  if (count < 1 || count > kMmGroupMax) return hipErrorInvalidValue;
+  MatmulArgs a{};
+  a.n = count;
+  int tiles = 0;
+  for (int j = 0; j < count; ++j) {
+    const MatmulJob &jb = jobs[j];
+    const int ncols = kDx ? jb.w.K : jb.w.N;
+    a.L[j] = jb.L;
+    a.Ln[j] = jb.Ln;
+    a.Rn[j] = jb.Rn;
+    a.keep[j] = jb.keep;
+    a.out[j] = jb.out;
+    a.w[j] = jb.w;
+    a.M[j] = jb.M;
+    a.r[j] = jb.r;
+    a.tcols[j] = (ncols + kBN - 1) / kBN;
+    a.t0[j] = tiles;
+    tiles += ((jb.M + kBM - 1) / kBM) * a.tcols[j];
+  }
+  a.t0[count] = tiles;
+  hipLaunchKernelGGL((k_matmul<kDx, kDrop>), dim3(tiles), dim3(kThreadsMM), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_matmul_fwd_group(int count, const MatmulJob *jobs, hipStream_t s) {
+  return launch_mm_group<false, false>(count, jobs, s);
+}
+
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s) {
   if (small_m_ok(M, r)) return launch_small_m_fwd(X, M, w, T, B, r, Y, s);
-  const int tiles = ((M + kBM - 1) / kBM) * ((w.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((k_matmul<false, false>), dim3(tiles), dim3(kThreadsMM), 0, s, X, M, w, T, B, r,
-                     static_cast<const uint32_t *>(nullptr), Y);
-  return hipGetLastError();
+  const MatmulJob job{X, T, B, nullptr, Y, w, M, r};
+  return launch_mm_group<false, false>(1, &job, s);
 }
 
 hipError_t launch_matmul_dx(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
                             const uint16_t *A, int r, uint16_t *dX, hipStream_t s) {
-  const int tiles = ((M + kBM - 1) / kBM) * ((w.K + kBN - 1) / kBN);
-  hipLaunchKernelGGL((k_matmul<true, false>), dim3(tiles), dim3(kThreadsMM), 0, s, dY, M, w, G, A, r,
-                     static_cast<const uint32_t *>(nullptr), dX);
-  return hipGetLastError();
+  const MatmulJob job{dY, G, A, nullptr, dX, w, M, r};
+  return launch_mm_group<true, false>(1, &job, s);
 }
 
 hipError_t launch_matmul_dx_drop(const uint16_t *dY, int M, const NF4View &w, const uint16_t *G,
                                  const uint16_t *A, int r, const uint32_t *keep, uint16_t *dX, hipStream_t s) {
-  const int tiles = ((M + kBM - 1) / kBM) * ((w.K + kBN - 1) / kBN);
-  hipLaunchKernelGGL((k_matmul<true, true>), dim3(tiles), dim3(kThreadsMM), 0, s, dY, M, w, G, A, r, keep, dX);
-  return hipGetLastError();
+  const MatmulJob job{dY, G, A, keep, dX, w, M, r};
+  return launch_mm_group<true, true>(1, &job, s);
 }
 
 }  // namespace qlora

@@ -16,7 +16,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._capi import LoraGradsDescStruct, NF4WeightStruct, check, lib
+from ._capi import LoraGradsDescStruct, MatmulFwdDescStruct, NF4WeightStruct, check, lib
 
 
 def _stream(t):
@@ -182,6 +182,33 @@ def dequantize_group(weights):
     sts = (NF4WeightStruct * len(weights))(*[w.struct() for w in weights])
     ptrs = (ctypes.c_void_p * len(weights))(*[_ptr(o) for o in outs])
     check(lib().qlora_dequantize_nf4_group(len(weights), sts, ptrs, _stream(outs[0])), "qlora_dequantize_nf4_group")
+    return outs
+
+
+def nf4_matmul_fwd_group(members):
+    """Y_i = X_i deq(W_i)^T + T_i B_i^T for up to 4 products sharing M in one
+    launch (qlora_nf4_matmul_fwd_group).  members: sequence of dicts with X,
+    w (NF4Weight), T, B and optional out.  Returns [Y, ...], bit-identical to
+    nf4_matmul_fwd of each."""
+    members = list(members)
+    if not 1 <= len(members) <= 4:
+        raise ValueError("a group holds 1 to 4 products")
+    descs, outs, structs = [], [], []
+    for i, mb in enumerate(members):
+        X, w, T, B = mb["X"], mb["w"], mb["T"], mb["B"]
+        M = _mat(X, "members[%d].X" % i)[0]
+        r = _mat(B, "members[%d].B" % i)[1]
+        _need(X, torch.bfloat16, "members[%d].X" % i, (M, w.cols))
+        _need(T, torch.bfloat16, "members[%d].T" % i, (M, r))
+        _need(B, torch.bfloat16, "members[%d].B" % i, (w.rows, r))
+        Y = _out(mb.get("out"), (M, w.rows), X.device, "members[%d].out" % i)
+        structs.append(w.struct())
+        outs.append(Y)
+        descs.append((X, M, T, B, r, Y))
+    arr = (MatmulFwdDescStruct * len(descs))(*[
+        MatmulFwdDescStruct(X.data_ptr(), M, ctypes.pointer(st), T.data_ptr(), B.data_ptr(), r, Y.data_ptr())
+        for (X, M, T, B, r, Y), st in zip(descs, structs)])
+    check(lib().qlora_nf4_matmul_fwd_group(len(descs), arr, _stream(members[0]["X"])), "qlora_nf4_matmul_fwd_group")
     return outs
 
 

@@ -284,7 +284,8 @@ size_t qlora_linear_group_workspace_bytes(int count, const qlora_linear_desc *de
  * that mixes 4-bit types runs its linears one call at a time.  At larger M,
  * linears whose descriptors carry the same X pointer and K (q, k, v; gate,
  * up) get their T from one qlora_lora_down_shared launch, then every linear
- * runs its fused matmul; results are bit-identical to single calls.  ws: device memory
+ * runs its fused matmul (in launches of up to 4 that share one tile space);
+ * results are bit-identical to single calls.  ws: device memory
  * of qlora_linear_group_workspace_bytes bytes, 16-byte aligned.  Validation of
  * every descriptor happens before any launch.  Pages: automatone.win,
  * "QLoRA paper explained", How it works; creativeworksofknowledge.com,
@@ -334,6 +335,28 @@ size_t qlora_lora_grad_in_workspace_bytes(int64_t N, int32_t r);
  * N % 8 == 0, 1 <= r <= 128. */
 int qlora_lora_grad_in(const uint16_t *dY, int64_t M, int64_t N, const uint16_t *B, int32_t r,
                        float scale, uint16_t *G, void *ws, size_t ws_bytes, void *stream);
+
+/* One product of qlora_nf4_matmul_fwd_group: the arguments of
+ * qlora_nf4_matmul_fwd. */
+typedef struct {
+  const uint16_t *X;
+  int64_t M;
+  const qlora_nf4_weight *W;
+  const uint16_t *T;
+  const uint16_t *B;
+  int32_t r;
+  uint16_t *Y;
+} qlora_matmul_fwd_desc;
+
+/* Up to 4 forward products that share M (for example q, k and v, or gate
+ * and up) in one launch over their concatenated tile grids: the last partial
+ * round of 256 x 256 tiles is shared instead of paid per product (gate and
+ * up at M = 8192: 2 x 1376 tiles, 11 rounds of 256 CUs instead of 12).  Each
+ * Y is bit-identical to qlora_nf4_matmul_fwd; decode-regime members
+ * (M <= 64, r % 8 == 0) run one call each.  Every member is validated before
+ * any launch; count outside 1..4, a NULL d or unequal M is INVALID_ARG.
+ * Pages: automatone.win, "QLoRA paper explained", How it works. */
+int qlora_nf4_matmul_fwd_group(int count, const qlora_matmul_fwd_desc *d, void *stream);
 
 /* dX [M, K] = dY deq(W) + G A with G = scale dY B [M, r] given.  No workspace. */
 int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W,

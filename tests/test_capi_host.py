@@ -249,6 +249,31 @@ def test_lora_grads_group_validation_and_workspace():
     assert L.qlora_lora_grads_group(1, zero, wsp, 1 << 30, None) == OK       # M = 0: nothing launched
 
 
+def test_matmul_fwd_group_validation():
+    L = q.lib()
+    Dm = _capi.MatmulFwdDescStruct
+    P = 0x20000
+    w1 = _fake_weight(11008, 4096)
+    w2 = _fake_weight(11008, 4096, 0x900000)
+    wk = _fake_weight(64, 100)                                  # K % 64 != 0
+    ds = (Dm * 2)(Dm(P, 8192, ctypes.pointer(w1), P, P, 64, P), Dm(P, 8192, ctypes.pointer(w2), P, P, 64, P))
+    assert L.qlora_nf4_matmul_fwd_group(0, ds, None) == INVALID
+    assert L.qlora_nf4_matmul_fwd_group(5, ds, None) == INVALID
+    assert L.qlora_nf4_matmul_fwd_group(2, None, None) == INVALID
+    uneq = (Dm * 2)(Dm(P, 8192, ctypes.pointer(w1), P, P, 64, P), Dm(P, 4096, ctypes.pointer(w2), P, P, 64, P))
+    assert L.qlora_nf4_matmul_fwd_group(2, uneq, None) == INVALID        # members must share M
+    badk = (Dm * 2)(Dm(P, 8192, ctypes.pointer(w1), P, P, 64, P), Dm(P, 8192, ctypes.pointer(wk), P, P, 64, P))
+    assert L.qlora_nf4_matmul_fwd_group(2, badk, None) == SHAPE
+    badr = (Dm * 1)(Dm(P, 8192, ctypes.pointer(w1), P, P, 129, P))
+    assert L.qlora_nf4_matmul_fwd_group(1, badr, None) == SHAPE
+    nox = (Dm * 2)(Dm(P, 8192, ctypes.pointer(w1), P, P, 64, P), Dm(None, 8192, ctypes.pointer(w2), P, P, 64, P))
+    assert L.qlora_nf4_matmul_fwd_group(2, nox, None) == INVALID
+    mis = (Dm * 1)(Dm(P, 8192, ctypes.pointer(w1), P, P, 64, 0x30008))
+    assert L.qlora_nf4_matmul_fwd_group(1, mis, None) == INVALID
+    zero = (Dm * 2)(Dm(None, 0, ctypes.pointer(w1), None, P, 64, None), Dm(None, 0, ctypes.pointer(w2), None, P, 64, None))
+    assert L.qlora_nf4_matmul_fwd_group(2, zero, None) == OK             # M = 0: nothing launched
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     W = torch.zeros(64, 64)
