@@ -131,9 +131,9 @@ struct SmGroup {
   SmLinear lin[kSmMaxGroup];
   int down_start[kSmMaxGroup + 1];
   int main_start[kSmMaxGroup + 1];
-  // Work plan of the GEMV kernel (set by launch_small_m_gemv): first item
-  // (row tile) and first chunk index (2048 columns of a tile) of each linear,
-  // chunks per tile.
+  // Work plan (set by launch_small_m_gemv and launch_small_m_stream): first
+  // item (row tile) of each linear, first unit of each linear (stream
+  // kernel) and the GEMV kernels' chunks per item.
   int item0[kSmMaxGroup + 1];
   int cost0[kSmMaxGroup + 1];
   int nch[kSmMaxGroup];

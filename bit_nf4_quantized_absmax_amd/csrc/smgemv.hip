@@ -4,10 +4,11 @@
 // (automatone.win, "QLoRA paper explained", How it works: the 4-bit weights
 // are dequantized on the fly for the math and never stored in 16-bit.)
 //
-// Work item = 4 weight rows x the whole K of one linear.  Items are split
-// over all waves of a persistent grid by equal byte counts (contiguous
-// ranges); every wave runs its items independently, so there is no
-// cross-wave reduction and no barrier after the set-up.  Per chunk of 2048
+// Work item = 4 weight rows x the whole K of one linear.  The items are dealt
+// round robin to the workgroups of a persistent grid, and the waves of a
+// workgroup claim its items one at a time; every wave runs each of its items
+// alone, so there is no cross-wave reduction and no barrier after the
+// set-up.  Per chunk of 2048
 // columns, lane l takes columns 32 l .. 32 l + 31: one 16-byte load per row
 // (a whole row segment per instruction, full cache lines), the block code and
 // group scale of its half-block, and the matching 32 bf16 of each token row
@@ -21,7 +22,8 @@
 // computes the current one.  When the X rows of the whole group fit next to
 // the table (kXL), they are copied into LDS once per workgroup (16 waves):
 // the per-step loads are then the weight stream alone and registers allow 16
-// waves per CU; T of every linear is formed there once too.  Otherwise (more
+// waves per CU; T is formed there once too.  The one-token kernel issues the
+// loads of X and T in the set-up before its first weight batch.  Otherwise (more
 // tokens, or X too large) X and the partials are loaded with each step
 // (8-wave workgroups).
 // The LoRA term T B^T (T = bf16(s * sum of the down-projection partials) or
@@ -61,17 +63,26 @@ __device__ __forceinline__ float gv_t8_level(int i) {
   return i >= 128 ? v : -v;
 }
 
-// Work plan in the kernel arguments (item0 / cost0 / nch / xoff of SmGroup).
-__device__ __forceinline__ int gv_first_item(const SmGroup &grp, int64_t lo) {
-  for (int i = 0; i < grp.n; ++i) {
-    const int tiles = grp.item0[i + 1] - grp.item0[i];
-    const int64_t last_start = grp.cost0[i] + static_cast<int64_t>(tiles - 1) * grp.nch[i];
-    if (lo <= last_start) {
-      const int64_t d = lo - grp.cost0[i];
-      return grp.item0[i] + (d <= 0 ? 0 : static_cast<int>((d + grp.nch[i] - 1) / grp.nch[i]));
-    }
-  }
-  return grp.item0[grp.n];
+// Work plan in the kernel arguments (item0 / nch of SmGroup): the linears
+// are ordered by chunks per item, most first; workgroup b of G takes items
+// b, b + G, b + 2 G, ..., so every workgroup gets the same mix of linears
+// and item lengths.  Its waves start on its first items and claim the next
+// one from an LDS counter when they start an item, so they finish within
+// about one item of each other (a fixed split over waves left some waves
+// with two 6-chunk items where others had one).  Every item is still
+// computed by one wave in chunk order: the results do not depend on which
+// wave takes it.
+__device__ __forceinline__ int gv_linear_of(const SmGroup &grp, int item) {
+  int li = 0;
+  while (li + 1 < grp.n && item >= grp.item0[li + 1]) ++li;
+  return li;
+}
+
+// Claims the next item of the workgroup (all lanes get the same value).
+__device__ __forceinline__ int gv_claim(int *counter, int lane) {
+  int v = 0;
+  if (lane == 0) v = atomicAdd(counter, 1);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -169,35 +180,36 @@ __global__ __launch_bounds__(kXL ? 1024 : 512) void k_sm_gemv(SmGroup grp) {
   __shared__ uint32_t sLut[256 * 64];   // word 64 * byte + lane: bf16x2 (NF4[lo], NF4[hi])
   __shared__ float sT8[256];
   __shared__ __attribute__((aligned(16))) uint8_t sX[kXL ? kGvXBytes : 16];
+  __shared__ int sNext;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int64_t total = grp.cost0[grp.n];
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
-  const int item_begin = gv_first_item(grp, total * gw / nw);
-  const int item_end = gv_first_item(grp, total * (gw + 1) / nw);
-  const bool active = item_begin < item_end;          // uniform per wave
+  // Items b, b + G, ... of the group for workgroup b, claimed by its waves
+  // as in k_sm_gemv1.
+  const int G = gridDim.x;
+  const int nitems = grp.item0[grp.n];
+  const int bid = blockIdx.x;
+  const int cnt = nitems > bid ? (nitems - 1 - bid) / G + 1 : 0;   // items of this workgroup
+  if (cnt == 0) return;                                // uniform per workgroup
+  const bool active = wave < cnt;                      // uniform per wave
 
-  auto linear_of = [&](int item) __attribute__((always_inline)) {
-    int li = 0;
-    while (li + 1 < grp.n && item >= grp.item0[li + 1]) ++li;
-    return li;
-  };
-  // Next step of this wave, or `st` itself at the end (a harmless repeat load).
+  // Next step of this wave, or `st` itself at the end (a harmless repeat
+  // load).  nxt: the index claimed when the current item started.
+  int nxt = cnt;
   auto advance = [&](const GvStep &st) __attribute__((always_inline)) {
     GvStep nx = st;
     if (st.c + 1 < grp.nch[st.li]) {
       ++nx.c;
-    } else if (st.item + 1 < item_end) {
-      ++nx.item;
+    } else if (nxt < cnt) {
+      nx.item = bid + G * nxt;
       nx.c = 0;
-      nx.li = linear_of(nx.item);
+      nx.li = gv_linear_of(grp, nx.item);
     }
     return nx;
   };
 
-  GvStep cur{item_begin, 0, linear_of(active ? item_begin : 0)};
+  const int first = active ? bid + G * wave : bid;
+  GvStep cur{first, 0, gv_linear_of(grp, first)};
   GvBatch<kM, kP, kXL> ba, bb;
   if (active) gv_load(grp, cur, lane, ba);            // first batch before the set-up below
 
@@ -210,6 +222,7 @@ __global__ __launch_bounds__(kXL ? 1024 : 512) void k_sm_gemv(SmGroup grp) {
       for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(lvt[j]));
     }
     if (threadIdx.x < 256) sT8[threadIdx.x] = gv_t8_level(threadIdx.x);
+    if (threadIdx.x == 0) sNext = kWaves;
     if constexpr (kXL) {
       // X (one token row: 80-byte groups of 32 bf16) and T of every linear.
       // X is copied in slots of 64 units of 16 bytes (one load instruction),
@@ -360,6 +373,7 @@ __global__ __launch_bounds__(kXL ? 1024 : 512) void k_sm_gemv(SmGroup grp) {
   // Two batches alternate: loads of step s + 1 are issued before step s is
   // consumed (a register copy would wait for them).
   auto step = [&](GvBatch<kM, kP, kXL> &now, GvBatch<kM, kP, kXL> &next) __attribute__((always_inline)) -> bool {
+    if (cur.c == 0) nxt = gv_claim(&sNext, lane);
     const GvStep nx = advance(cur);
     const bool more = nx.item != cur.item || nx.c != cur.c;
     gv_load(grp, nx, lane, next);
@@ -390,6 +404,14 @@ __device__ __forceinline__ void gv1_load(const SmGroup &grp, const GvStep &st, i
   const int n0 = (st.item - grp.item0[st.li]) * kGvRows;
   const int k0 = st.c * kGvChunk + 32 * lane;
   const int kc = k0 < K ? k0 : K - 32;
+  // B first: it is used only on an item's last chunk, so on other steps its
+  // registers are free for the compiler to reuse, which waits for the load
+  // that writes them; as the oldest load of the batch that wait is short.
+  {
+    const int64_t n = min(n0 + (lane >> 4), N - 1);
+    const int j = 8 * (lane & 15);
+    b.bq = *reinterpret_cast<const uint4 *>(L.B + n * r + (j < r ? j : 0));
+  }
 #pragma unroll
   for (int i = 0; i < kGvRows; ++i) {
     const int64_t n = min(n0 + i, N - 1);
@@ -406,11 +428,6 @@ __device__ __forceinline__ void gv1_load(const SmGroup &grp, const GvStep &st, i
     const int64_t g = ((n * KB + st.c * kGvChunk / 64) >> 8) + (lane & 1);
     b.c2v = L.w.c2[min(g, nb2 - 1)];
   }
-  {
-    const int64_t n = min(n0 + (lane >> 4), N - 1);
-    const int j = 8 * (lane & 15);
-    b.bq = *reinterpret_cast<const uint4 *>(L.B + n * r + (j < r ? j : 0));
-  }
 }
 
 template <bool kP>
@@ -422,6 +439,8 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
     uint32_t lut[256 * 64];   // word 64 * byte + lane: bf16x2 (NF4[lo], NF4[hi])
     float t8[256];
     uint8_t x[kGvXBytes];
+    float mean[kSmMaxGroup];  // each linear's constant mean
+    int next;                 // the workgroup's next unclaimed item
   } sm;
   uint32_t *const sLut = sm.lut;
   float *const sT8 = sm.t8;
@@ -429,44 +448,44 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int64_t total = grp.cost0[grp.n];
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
-  const int item_begin = gv_first_item(grp, total * gw / nw);
-  const int item_end = gv_first_item(grp, total * (gw + 1) / nw);
-  const bool active = item_begin < item_end;          // uniform per wave
+  // Workgroup b takes items b, b + G, b + 2 G, ... (G workgroups): every
+  // workgroup gets the same mix of linears and of item lengths.  Its waves
+  // start on its first 16 items and claim the next one from an LDS counter
+  // whenever they start an item (the linears are ordered longest item first,
+  // so the long items go first).
+  const int G = gridDim.x;
+  const int nitems = grp.item0[grp.n];
+  const int bid = blockIdx.x;
+  const int cnt = nitems > bid ? (nitems - 1 - bid) / G + 1 : 0;   // items of this workgroup
+  if (cnt == 0) return;                                // uniform per workgroup
+  const bool active = wave < cnt;                      // uniform per wave
 
-  auto linear_of = [&](int item) __attribute__((always_inline)) {
-    int li = 0;
-    while (li + 1 < grp.n && item >= grp.item0[li + 1]) ++li;
-    return li;
-  };
+  int nxt = cnt;                                       // index claimed when the current item started
   auto advance = [&](const GvStep &st) __attribute__((always_inline)) {
     GvStep nx = st;
     if (st.c + 1 < grp.nch[st.li]) {
       ++nx.c;
-    } else if (st.item + 1 < item_end) {
-      ++nx.item;
+    } else if (nxt < cnt) {
+      nx.item = bid + G * nxt;
       nx.c = 0;
-      nx.li = linear_of(nx.item);
+      nx.li = gv_linear_of(grp, nx.item);
     }
     return nx;
   };
 
-  GvStep cur{item_begin, 0, linear_of(active ? item_begin : 0)};
+  const int first = active ? bid + G * wave : bid;
+  GvStep cur{first, 0, gv_linear_of(grp, first)};
   Gv1Batch ba, bb;
-  if (active) gv1_load(grp, cur, lane, ba);           // first batch before the set-up below
 
-  // Tables, X and T into LDS (all loads first, then the stores: one latency,
-  // overlapping the first weight batch).
+  // Set-up: the first weight batch, then the X and T loads, go out before
+  // anything waits (storing X and T then waits for the batch too: loads
+  // complete in order).  The X copy's slot bounds are read once, so that
+  // finding a slot's linear needs no memory round trip.
   {
-    const uint32_t *lvt = cGvQ4Level + 16 * grp.lin[0].w.qtype;   // one 4-bit type per group
-    for (int e = wave; e < 16; e += kWaves) {
-      const float lo = u2f(lvt[e]);
+    if (active) gv1_load(grp, cur, lane, ba);
+    int xs[kSmMaxGroup + 1];                           // slot bounds of the linears' X copies
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(lvt[j]));
-    }
-    if (threadIdx.x < 256) sT8[threadIdx.x] = gv_t8_level(threadIdx.x);
+    for (int i = 0; i <= kSmMaxGroup; ++i) xs[i] = grp.xs0[i];
     uint4 xr[kGvXJ];
     int xdst[kGvXJ];
 #pragma unroll
@@ -474,51 +493,69 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
       const int slot = wave + kWaves * j;
       xdst[j] = -1;
       xr[j] = make_uint4(0, 0, 0, 0);
-      if (slot < grp.xs0[grp.n]) {
+      if (slot < xs[grp.n]) {
         int li = 0;
-        while (li + 1 < grp.n && slot >= grp.xs0[li + 1]) ++li;
+#pragma unroll
+        for (int i = 1; i < kSmMaxGroup; ++i) li += (i < grp.n && slot >= xs[i]) ? 1 : 0;
         const SmLinear &L = grp.lin[li];
         const int units = L.w.K >> 3;
-        const int unit = (slot - grp.xs0[li]) * 64 + lane;
+        const int unit = (slot - xs[li]) * 64 + lane;
         xr[j] = reinterpret_cast<const uint4 *>(L.X)[min(unit, units - 1)];
         if (unit < units) xdst[j] = grp.xoff[li] + (unit >> 2) * kGvXGroup + (unit & 3) * 16;
       }
     }
-    uint32_t tv = 0u;
-    int tdst = -1, tj = 0;
-    uint16_t *tout = nullptr;
-    if (wave < grp.n) {
+    // T of linear w from wave w: its partial slices (or T as given).
+    const int tj = 2 * lane;
+    const bool tact = wave < grp.n && tj < grp.lin[wave < grp.n ? wave : 0].r;
+    float2 pv[kP ? kGvPSX : 1];
+    uint32_t tin = 0u;
+    if (tact) {
       const SmLinear &L = grp.lin[wave];
-      tj = 2 * lane;
-      if (tj < L.r) {
-        if constexpr (kP) {
-          float2 pv[kGvPSX];
+      if constexpr (kP) {
 #pragma unroll
-          for (int s2 = 0; s2 < kGvPSX; ++s2)
-            pv[s2] = *reinterpret_cast<const float2 *>(L.P + static_cast<int64_t>(min(s2, L.S - 1)) * L.r + tj);
-          float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < kGvPSX; ++s2) {
-            const bool on = s2 < L.S;
-            t0 += on ? pv[s2].x : 0.f;
-            t1 += on ? pv[s2].y : 0.f;
-          }
-          tv = pack_bf16x2(L.scale * t0, L.scale * t1);
-        } else {
-          tv = *reinterpret_cast<const uint32_t *>(L.Tin + tj);
-        }
-        tdst = grp.toff[wave] + 2 * tj;
-        if (blockIdx.x == 0) tout = L.Tout;
+        for (int s2 = 0; s2 < kGvPSX; ++s2)
+          pv[s2] = *reinterpret_cast<const float2 *>(L.P + static_cast<int64_t>(min(s2, L.S - 1)) * L.r + tj);
+      } else {
+        tin = *reinterpret_cast<const uint32_t *>(L.Tin + tj);
       }
+    }
+
+    const uint32_t *lvt = cGvQ4Level + 16 * grp.lin[0].w.qtype;   // one 4-bit type per group
+    for (int e = wave; e < 16; e += kWaves) {
+      const float lo = u2f(lvt[e]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sLut[64 * (e + 16 * j) + lane] = pack_bf16x2(lo, u2f(lvt[j]));
+    }
+    if (threadIdx.x < 256) sT8[threadIdx.x] = gv_t8_level(threadIdx.x);
+    if (threadIdx.x == 0) sm.next = kWaves;
+    // The means come from LDS in the step loop: a global load there would be
+    // the youngest load when the step waits, and waiting for it would also
+    // wait for the next batch.
+    if (threadIdx.x < grp.n) sm.mean[threadIdx.x] = grp.lin[threadIdx.x].w.mean[0];
+    if (tact) {
+      const SmLinear &L = grp.lin[wave];
+      uint32_t tv = tin;
+      if constexpr (kP) {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kGvPSX; ++s2) {
+          const bool on = s2 < L.S;
+          t0 += on ? pv[s2].x : 0.f;
+          t1 += on ? pv[s2].y : 0.f;
+        }
+        tv = pack_bf16x2(L.scale * t0, L.scale * t1);
+      }
+      *reinterpret_cast<uint32_t *>(sX + grp.toff[wave] + 2 * tj) = tv;
+      if (bid == 0 && L.Tout) *reinterpret_cast<uint32_t *>(L.Tout + tj) = tv;
     }
 #pragma unroll
     for (int j = 0; j < kGvXJ; ++j)
       if (xdst[j] >= 0) *reinterpret_cast<uint4 *>(sX + xdst[j]) = xr[j];
-    if (tdst >= 0) {
-      *reinterpret_cast<uint32_t *>(sX + tdst) = tv;
-      if (tout) *reinterpret_cast<uint32_t *>(tout + tj) = tv;
-    }
   }
+  // Storing X waited for the first batch already (loads complete in order);
+  // saying so here leaves no load of the set-up outstanding at the loop, so
+  // that the compiler's waits in the loop count only the loop's own batches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
   __syncthreads();
   if (!active) return;                                  // no barrier follows
 
@@ -532,7 +569,7 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
     const int k0 = st.c * kGvChunk + 32 * lane;
     const bool kin = k0 < K;                            // K % 64 == 0: all 32 columns or none
     const int kc = kin ? k0 : K - 32;
-    const float mean = L.w.mean[0];
+    const float mean = sm.mean[st.li];
     const int n0 = (st.item - grp.item0[st.li]) * kGvRows;
     uint4 xl[4];
     const uint8_t *xp = sX + grp.xoff[st.li] + (kc >> 5) * kGvXGroup;
@@ -570,8 +607,13 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
     }
     if (st.c + 1 < grp.nch[st.li]) return;
     // Last chunk of the item: LoRA term (lane: row lane / 16, adapter columns
-    // 8 (lane % 16) .. +7), wave sums, stores.
-    const int j = 8 * (lane & 15);
+    // 8 (lane % 16) .. +7), wave sums, stores.  The lane index goes through an
+    // empty asm so that its T address is formed here: hoisted out of the step
+    // loop it would be spilled, and reloading a spill waits for every load in
+    // flight, the next batch included.
+    int lj = lane;
+    asm volatile("" : "+v"(lj));
+    const int j = 8 * (lj & 15);
     float lp = 0.f;
     if (j < r) {
       const uint4 tq = *reinterpret_cast<const uint4 *>(sX + grp.toff[st.li] + 2 * j);
@@ -591,9 +633,13 @@ __global__ __launch_bounds__(1024) void k_sm_gemv1(SmGroup grp) {
   };
 
   auto step = [&](Gv1Batch &now, Gv1Batch &next) __attribute__((always_inline)) -> bool {
+    if (cur.c == 0) nxt = gv_claim(&sm.next, lane);
     const GvStep nx = advance(cur);
     const bool more = nx.item != cur.item || nx.c != cur.c;
     gv1_load(grp, nx, lane, next);
+    // All of the next batch is issued before this one is consumed: moving
+    // the consumption up would wait for this batch before the next is out.
+    __builtin_amdgcn_sched_barrier(0);
     compute(cur, now);
     cur = nx;
     return more;
@@ -688,18 +734,20 @@ static void gv_launch(bool p, int grid, const SmGroup &grp, hipStream_t s) {
 }
 
 hipError_t launch_small_m_gemv(SmGroup &grp, hipStream_t s) {
+  // Linears with more chunks per item first (stable), so that a workgroup
+  // whose range spans two linears starts on the longer items.
+  auto chunks = [](const SmLinear &L) { return (L.w.K + kGvChunk - 1) / kGvChunk; };
+  for (int i = 1; i < grp.n; ++i)
+    for (int j = i; j > 0 && chunks(grp.lin[j]) > chunks(grp.lin[j - 1]); --j) std::swap(grp.lin[j], grp.lin[j - 1]);
   int items = 0;
-  int64_t cost = 0, xbytes = 0, tbytes = 0;
+  int64_t xbytes = 0;
   for (int i = 0; i < grp.n; ++i) {
     const int tiles = (grp.lin[i].w.N + kGvRows - 1) / kGvRows;
     grp.item0[i] = items;
-    grp.cost0[i] = static_cast<int>(cost);
     grp.nch[i] = (grp.lin[i].w.K + kGvChunk - 1) / kGvChunk;
     grp.xoff[i] = static_cast<int>(xbytes);
     items += tiles;
-    cost += static_cast<int64_t>(tiles) * grp.nch[i];
     xbytes += static_cast<int64_t>(grp.M) * (grp.lin[i].w.K >> 5) * kGvXGroup;
-    tbytes += static_cast<int64_t>(grp.M) * grp.lin[i].r * 2;
   }
   {
     int64_t t = xbytes;
@@ -713,9 +761,7 @@ hipError_t launch_small_m_gemv(SmGroup &grp, hipStream_t s) {
     grp.xs0[grp.n] = xs;
   }
   grp.item0[grp.n] = items;
-  grp.cost0[grp.n] = static_cast<int>(cost);
   const bool xl = small_m_gemv_xl(grp);
-  (void)tbytes;
   const int cus = gv_cu_count();
   // kXL: one 16-wave workgroup per CU; else two 8-wave workgroups per CU.
   const int waves = xl ? 16 : 8;
