@@ -7,15 +7,20 @@ N(0, 0.02) quantized to NF4 with double-quantized constants, 8192 tokens of
 bf16 activations N(0, 1), LoRA r = 64, alpha = 16 on every linear.  One step
 is the forward and the backward (dX, dA, dB) of all seven linears with the
 weights already quantized and every input resident in HBM:
-    T = X A^T;  Y = X deq(W)^T + s T B^T;  G = dY B;
-    dX = dY deq(W) + s G A;  dA = s G^T X;  dB = s dY^T T.
+    W~ = deq(W);  T = X A^T;  Y = X W~^T + s T B^T;  G = dY B;
+    dX = dY W~ + s G A;  dA = s G^T X;  dB = s dY^T T.
+By default (--matmul deq) the step dequantizes the layer's seven weights to
+bf16 in one grouped launch (timed, part of the step) and both matmuls of each
+linear read those copies; --matmul fused expands the NF4 codes inside every
+matmul tile instead.  The outputs of the two are bit-identical.
 Metric: algorithmic TFLOP/s = sum over linears of 4 M N K + 6 M r (N + K)
 per step, divided by the mean step time of the timed steps (HIP events on
 the launch stream; step_ms gives the median and minimum single step).
 
 Also reported on the same JSON line:
-  roofline      the dominant kernel (fused dequant matmul), timed with HIP
+  roofline      the dominant kernel (the forward matmul), timed with HIP
                 events around each of its launches inside the timed region
+  kernels       the same for the dX matmul and the dequantization
   cpu_baseline  the CPU oracle on a bounded token sample of the same step
   small_m       forward-only M = 1 / 16 / 64 over 4 weight sets (> the 256 MB
                 Infinity Cache), replayed from HIP graphs (200 replays, mean,
@@ -37,7 +42,7 @@ Also reported on the same JSON line:
                 quantized, with the codec oracle timed on one of its weights
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extras]
-                       [--copy-probe-mib MiB] [--small-m-only [--small-m-eager]]
+                       [--matmul deq|fused] [--copy-probe-mib MiB] [--small-m-only [--small-m-eager]]
 """
 
 import argparse
@@ -73,6 +78,9 @@ def parse():
     p.add_argument("--codec-only", action="store_true",
                    help="only the quantize / dequantize figures, as one JSON line (for profiling the codec)")
     p.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle")
+    p.add_argument("--matmul", choices=("deq", "fused"), default="deq",
+                   help="deq: one grouped dequantize per step, then the matmuls from the bf16 weights; "
+                        "fused: the NF4 codes expanded inside every matmul tile")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB first (a reference "
                         "dispatch for scaling hardware byte counters)")
@@ -139,6 +147,7 @@ class Layer:
         self.T = torch.empty(M, r, dtype=bf, device=dev)
         self.G = torch.empty(M, r, dtype=bf, device=dev)
         self.dX = torch.empty(M, K, dtype=bf, device=dev)
+        self.Wd = torch.empty(N, K, dtype=bf, device=dev)   # the step's dequantized weight
         ws = q.lib().qlora_lora_grads_workspace_bytes(M, N, K, r)
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.gws = torch.empty(max(q.lib().qlora_lora_grad_in_workspace_bytes(N, r), 16), dtype=torch.uint8,
@@ -161,30 +170,50 @@ def fwd_groups(layers):
     return [[L] for L in layers]
 
 
-def run_step(q, torch, layers, scale, events=None):
-    """One fwd + bwd of every linear: per forward group the LoRA-down of each
-    member, the group's fused forward matmuls (one launch), then per member
-    G, the fused dX matmul and dA / dB."""
+def _timed(events, key, torch, grp):
+    if events is None:
+        return None
+    events.setdefault(key, []).append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                                       grp))
+    events[key][-1][0].record()
+    return events[key][-1][1]
+
+
+def run_step(q, torch, layers, scale, events=None, mode="deq"):
+    """One fwd + bwd of every linear.  mode "deq": the layer's weights are
+    dequantized to bf16 once (one grouped launch) and both matmuls of every
+    linear read those copies; "fused": the matmuls expand the NF4 codes
+    themselves.  Per forward group: the LoRA-down of each member, the group's
+    forward matmuls (one launch); then per member G, the dX matmul and
+    dA / dB."""
+    if mode == "deq":
+        for i in range(0, len(layers), 8):
+            part = layers[i:i + 8]
+            end = _timed(events, "dequant", torch, part)
+            q.dequantize_group([L.w for L in part], outs=[L.Wd for L in part])
+            if end is not None:
+                end.record()
     for grp in fwd_groups(layers):
         for L in grp:
             q.lora_down(L.X, L.A, scale, out=L.T)
-        if events is not None:
-            events["fwd"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), grp))
-            events["fwd"][-1][0].record()
-        if len(grp) > 1:
+        end = _timed(events, "fwd", torch, grp)
+        if mode == "deq":
+            q.deq_matmul_fwd_group([dict(X=L.X, Wd=L.Wd, T=L.T, B=L.B, out=L.Y) for L in grp])
+        elif len(grp) > 1:
             q.nf4_matmul_fwd_group([dict(X=L.X, w=L.w, T=L.T, B=L.B, out=L.Y) for L in grp])
         else:
             q.nf4_matmul_fwd(grp[0].X, grp[0].w, grp[0].T, grp[0].B, out=grp[0].Y)
-        if events is not None:
-            events["fwd"][-1][1].record()
+        if end is not None:
+            end.record()
         for L in grp:
             q.lora_grad_in(L.dY, L.B, scale, out=L.G, workspace=L.gws)
-            if events is not None:
-                events["dx"].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), [L]))
-                events["dx"][-1][0].record()
-            q.nf4_matmul_dx(L.dY, L.w, L.G, L.A, out=L.dX)
-            if events is not None:
-                events["dx"][-1][1].record()
+            end = _timed(events, "dx", torch, [L])
+            if mode == "deq":
+                q.deq_matmul_dx(L.dY, L.Wd, L.G, L.A, out=L.dX)
+            else:
+                q.nf4_matmul_dx(L.dY, L.w, L.G, L.A, out=L.dX)
+            if end is not None:
+                end.record()
             q.lora_grads(L.X, L.dY, L.G, L.T, workspace=L.ws)
 
 
@@ -553,18 +582,18 @@ def dropout_bench(q, torch, workloads, cfg, dev, p=0.05, steps=5):
                 note="composite calls (workspaces allocated by the Python binding each call)")
 
 
-def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3):
+def layer_bench(q, torch, workloads, cfg, dev, tokens, warmup=1, steps=3, mode="deq"):
     """fwd + bwd of all linears of one layer of `cfg` at `tokens` tokens."""
     layers = [Layer(q, torch, workloads, lin, tokens, cfg.rank, 1000 * cfg.index + 10 * i, dev)
               for i, lin in enumerate(cfg.linears)]
     flops = sum(L.flops for L in layers)
     for _ in range(warmup):
-        run_step(q, torch, layers, cfg.scale)
+        run_step(q, torch, layers, cfg.scale, mode=mode)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        run_step(q, torch, layers, cfg.scale)
+        run_step(q, torch, layers, cfg.scale, mode=mode)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -772,7 +801,7 @@ def main():
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        run_step(q, torch, layers, scale)
+        run_step(q, torch, layers, scale, mode=args.matmul)
     torch.cuda.synchronize()
     log("warmup done; timing %d steps" % args.steps)
 
@@ -781,7 +810,7 @@ def main():
     gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     gev[0].record()
     for i in range(args.steps):
-        run_step(q, torch, layers, scale, events)
+        run_step(q, torch, layers, scale, events, mode=args.matmul)
         gev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -793,13 +822,21 @@ def main():
     kern = {}
     for key, evs in events.items():
         tot_ms = sum(a.elapsed_time(b) for a, b, _ in evs)
+        if key == "dequant":   # HBM-bound: algorithmic bytes (codes, constants, mean read; bf16 written)
+            nbytes = sum(L.w.nbytes() + 2 * L.N * L.K for _, _, grp in evs for L in grp)
+            kern[key] = dict(launches=len(evs), avg_us=tot_ms * 1e3 / len(evs), bytes_per_launch=nbytes / len(evs),
+                             total_ms=tot_ms)
+            continue
         flops = sum((L.fwd_mm_flops if key == "fwd" else L.dx_mm_flops) for _, _, grp in evs for L in grp)
         kern[key] = dict(launches=len(evs), avg_us=tot_ms * 1e3 / len(evs),
                          flops_per_launch=flops / len(evs), total_ms=tot_ms)
-    dom_key = max(kern, key=lambda k: kern[k]["total_ms"])
+    dom_key = max((k for k in kern if k != "dequant"), key=lambda k: kern[k]["total_ms"])
     dom = kern[dom_key]
     achieved = dom["flops_per_launch"] / (dom["avg_us"] * 1e-6) / 1e12
-    dom_kernel = "qlora::k_matmul<false, false>" if dom_key == "fwd" else "qlora::k_matmul<true, false>"
+    if args.matmul == "deq":
+        dom_kernel = "qlora::k_matmul_pre<false>" if dom_key == "fwd" else "qlora::k_matmul_pre<true>"
+    else:
+        dom_kernel = "qlora::k_matmul<false, false>" if dom_key == "fwd" else "qlora::k_matmul<true, false>"
     roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=recorded_traffic(dom_kernel),
                     traffic_unit="HBM bytes per launch (PMC FETCH_SIZE + WRITE_SIZE, copy-scaled), recorded in "
@@ -808,8 +845,15 @@ def main():
                     kernel=dom_kernel + (" (forward)" if dom_key == "fwd" else " (dX)"),
                     avg_launch_us=round(dom["avg_us"], 2),
                     flops_per_launch=dom["flops_per_launch"])
-    other = {k: dict(avg_us=round(v["avg_us"], 2), TFLOPs=round(v["flops_per_launch"] / (v["avg_us"] * 1e-6) / 1e12, 1),
-                     share_of_step=round(v["total_ms"] / args.steps / ms_step, 3)) for k, v in kern.items()}
+    other = {}
+    for k, v in kern.items():
+        rec = dict(avg_us=round(v["avg_us"], 2), launches_per_step=v["launches"] // args.steps,
+                   share_of_step=round(v["total_ms"] / args.steps / ms_step, 3))
+        if "flops_per_launch" in v:
+            rec["TFLOPs"] = round(v["flops_per_launch"] / (v["avg_us"] * 1e-6) / 1e12, 1)
+        else:
+            rec["GBps"] = round(v["bytes_per_launch"] / (v["avg_us"] * 1e-6) / 1e9, 1)
+        other[k] = rec
 
     extras = {}
     if not args.no_extras:
@@ -864,6 +908,9 @@ def main():
         "config": {"workload": "llama7b_layer_7linears_fwd_bwd", "tokens": cfg.tokens, "rank": cfg.rank,
                    "alpha": cfg.alpha, "step_flops": step_flops,
                    "shapes": "q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008 (N x K)",
+                   "matmul": ("the layer's 7 weights dequantized to bf16 once per step (one grouped launch, "
+                              "timed), both matmuls reading those copies" if args.matmul == "deq" else
+                              "NF4 codes expanded inside every matmul tile"),
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": other,

@@ -24,7 +24,7 @@ EXPORTED = (
     "qlora_quantize_group_workspace_bytes", "qlora_quantize_nf4_group", "qlora_dequantize_nf4_group",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_bwd",
     "qlora_lora_down", "qlora_nf4_matmul_fwd", "qlora_nf4_matmul_fwd_group", "qlora_lora_grad_in_workspace_bytes", "qlora_lora_grad_in",
-    "qlora_nf4_matmul_dx",
+    "qlora_nf4_matmul_dx", "qlora_deq_matmul_fwd", "qlora_deq_matmul_fwd_group", "qlora_deq_matmul_dx",
     "qlora_lora_grads_workspace_bytes", "qlora_lora_grads",
     "qlora_lora_grads_group_workspace_bytes", "qlora_lora_grads_group",
     "qlora_linear_group_workspace_bytes", "qlora_linear_fwd_group",
@@ -77,6 +77,20 @@ class MatmulFwdDescStruct(ctypes.Structure):
     ]
 
 
+class DeqMatmulFwdDescStruct(ctypes.Structure):
+    _fields_ = [
+        ("X", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("Wd", ctypes.c_void_p),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("T", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("r", ctypes.c_int32),
+        ("Y", ctypes.c_void_p),
+    ]
+
+
 class LoraGradsDescStruct(ctypes.Structure):
     _fields_ = [
         ("X", ctypes.c_void_p),
@@ -119,6 +133,9 @@ _SIGS = {
     "qlora_lora_grad_in_workspace_bytes": (_sz, [_i64, _i32]),
     "qlora_lora_grad_in": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
     "qlora_nf4_matmul_dx": (ctypes.c_int, [_vp, _i64, _wp, _vp, _vp, _i32, _vp, _vp]),
+    "qlora_deq_matmul_fwd": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp]),
+    "qlora_deq_matmul_fwd_group": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(DeqMatmulFwdDescStruct), _vp]),
+    "qlora_deq_matmul_dx": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp]),
     "qlora_lora_grads_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "qlora_lora_grads": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]),
     "qlora_lora_grads_group_workspace_bytes": (_sz, [ctypes.c_int, ctypes.POINTER(LoraGradsDescStruct)]),

@@ -45,6 +45,18 @@ int check_linear_shape(int64_t M, const qlora_nf4_weight *w, int32_t r, float sc
 
 bool bf16_ok(const void *p) { return p && aligned(p, 16); }
 bool bf16_opt(const void *p) { return !p || aligned(p, 16); }
+
+// Shape rules of the products from a dequantized weight Wd [N, K]: those of
+// the fused kernels, and N % 64 == 0 for dX (its contraction over N has no
+// zero-padded tail on this route).
+int check_deq_shape(int64_t M, const uint16_t *Wd, int64_t N, int64_t K, int32_t r, bool dx) {
+  if (M < 0 || N < 1 || K < 1 || !bf16_ok(Wd)) return QLORA_ERR_INVALID_ARG;
+  if (K % 64 != 0 || N % (dx ? 64 : 8) != 0) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (N > kMaxElems / K) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (r < 1 || r > 128) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  if (M > 0 && (M > kMaxElems / std::max(N, K))) return QLORA_ERR_UNSUPPORTED_SHAPE;
+  return QLORA_OK;
+}
 // A tensor with M rows: at M = 0 it has no storage and its pointer may be NULL.
 bool rows_ok(const void *p, int64_t M) { return M == 0 ? bf16_opt(p) : bf16_ok(p); }
 
@@ -317,6 +329,42 @@ int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W
   if (M == 0) return QLORA_OK;
   return from_hip(launch_matmul_dx(dY, static_cast<int>(M), view_of(W), G, A, r, dX,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int qlora_deq_matmul_fwd(const uint16_t *X, int64_t M, const uint16_t *Wd, int64_t N, int64_t K, const uint16_t *T,
+                         const uint16_t *B, int32_t r, uint16_t *Y, void *stream) {
+  const qlora_deq_matmul_fwd_desc d{X, M, Wd, N, K, T, B, r, Y};
+  return qlora_deq_matmul_fwd_group(1, &d, stream);
+}
+
+int qlora_deq_matmul_fwd_group(int count, const qlora_deq_matmul_fwd_desc *d, void *stream) {
+  if (count < 1 || count > 4 || !d) return QLORA_ERR_INVALID_ARG;
+  const int64_t M = d[0].M;
+  for (int i = 0; i < count; ++i) {
+    if (d[i].M != M) return QLORA_ERR_INVALID_ARG;
+    int st = check_deq_shape(M, d[i].Wd, d[i].N, d[i].K, d[i].r, false);
+    if (st) return st;
+    if (!rows_ok(d[i].X, M) || !rows_ok(d[i].T, M) || !bf16_ok(d[i].B) || !rows_ok(d[i].Y, M))
+      return QLORA_ERR_INVALID_ARG;
+  }
+  if (M == 0) return QLORA_OK;
+  MatmulJob jobs[4];
+  for (int i = 0; i < count; ++i) {
+    const NF4View shape{nullptr, nullptr, nullptr, nullptr, static_cast<int>(d[i].N), static_cast<int>(d[i].K), 0};
+    jobs[i] = MatmulJob{d[i].X, d[i].T, d[i].B, nullptr, d[i].Y, shape, static_cast<int>(M), d[i].r, d[i].Wd};
+  }
+  return from_hip(launch_pre_matmul_fwd_group(count, jobs, static_cast<hipStream_t>(stream)));
+}
+
+int qlora_deq_matmul_dx(const uint16_t *dY, int64_t M, const uint16_t *Wd, int64_t N, int64_t K, const uint16_t *G,
+                        const uint16_t *A, int32_t r, uint16_t *dX, void *stream) {
+  int st = check_deq_shape(M, Wd, N, K, r, true);
+  if (st) return st;
+  if (!rows_ok(dY, M) || !rows_ok(G, M) || !bf16_ok(A) || !rows_ok(dX, M)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  const NF4View shape{nullptr, nullptr, nullptr, nullptr, static_cast<int>(N), static_cast<int>(K), 0};
+  const MatmulJob job{dY, G, A, nullptr, dX, shape, static_cast<int>(M), r, Wd};
+  return from_hip(launch_pre_matmul_dx(job, static_cast<hipStream_t>(stream)));
 }
 
 size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {

@@ -65,10 +65,16 @@ struct MatmulJob {
   NF4View w;
   int M;
   int r;
+  const uint16_t *wd = nullptr;   // dequantized bf16 weight [w.N, w.K] (the pre-dequantized kernels)
 };
 // Up to 4 forward products (M >= 65 each) in one launch over their
 // concatenated tile grids; each output as launch_matmul_fwd computes it.
 hipError_t launch_matmul_fwd_group(int count, const MatmulJob *jobs, hipStream_t s);
+// The same products from dequantized bf16 weights (job.wd; only w.N and w.K
+// of job.w are read): forward groups of up to 4, and dX (w.N % 64 == 0).
+// Outputs are bit-identical to the fused kernels' on the same weight.
+hipError_t launch_pre_matmul_fwd_group(int count, const MatmulJob *jobs, hipStream_t s);
+hipError_t launch_pre_matmul_dx(const MatmulJob &job, hipStream_t s);
 // Y [M, N] = X deq(W)^T + T B^T
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s);

@@ -66,6 +66,7 @@ struct MatmulArgs {
   const uint32_t *keep[kMmGroupMax];
   uint16_t *out[kMmGroupMax];
   NF4View w[kMmGroupMax];
+  const uint16_t *wd[kMmGroupMax];   // dequantized bf16 weight [N, K] (k_matmul_pre; N and K from w)
   int M[kMmGroupMax];
   int r[kMmGroupMax];
   int tcols[kMmGroupMax];
@@ -304,6 +305,73 @@ __device__ __forceinline__ void load_a_tile(uint8_t *stage, const uint16_t *A, i
   }
 }
 
+// Dequantized dX weight tile: rows n0 .. n0+63 (clamped to N - 1) and
+// columns k0 .. k0+255 (16-byte chunks clamped to the row's last) of a
+// row-major bf16 [N, K] matrix, DMA'd into the [64 n][256 k] swz512 layout.
+// Wave w issues the 1 KB instructions 4 w .. 4 w + 3 (two 512-byte rows
+// each); lane i of an instruction lands in slot i (row 2 u + i / 32,
+// position i % 32).
+__device__ __forceinline__ void dma_wdx(uint8_t *stage, const uint16_t *W, int N, int K, int n0, int k0, int wave,
+                                        int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int u = wave * 4 + j;
+    const int row = 2 * u + (lane >> 5);
+    const int chunk = (lane & 31) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+    const int grow = min(n0 + row, N - 1);
+    const int gcol = min(k0 + chunk * 8, K - 8);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage) + u * 1024);
+    dma16(W + static_cast<int64_t>(grow) * K + gcol, dst);
+  }
+}
+
+// The LoRA contraction steps of a tile: left = Ln [M, r] (T or G), right =
+// B [N, r] (forward) or A [r, K] (dX), 64 adapter columns per step.
+template <bool kDx>
+__device__ __forceinline__ void lora_tile_steps(uint8_t *xs, uint8_t *ws, const uint16_t *Ln, const uint16_t *Rn,
+                                                int r, int M, int N, int K, int m0, int c0, const OpOffsets &ops,
+                                                f32x16_t (&acc)[4][2]) {
+  for (int j0 = 0; j0 < r; j0 += kBK) {
+    load_narrow(xs, Ln, r, m0, M, j0);
+    if (kDx)
+      load_a_tile(ws, Rn, r, K, j0, c0);
+    else
+      load_narrow(ws, Rn, r, c0, N, j0);
+    __syncthreads();
+    mfma_stage<kDx>(xs, ws, ops, acc);
+    __syncthreads();
+  }
+}
+
+// Epilogue: the wave's 128 x 64 block as bf16 into its own 16 KB region of
+// the stages (16-byte chunks XOR-swizzled by row), then 16-byte stores
+// guarded by the matrix bounds (ncols % 8 == 0).  MFMA 32x32 output layout:
+// lane l holds column l % 32; element e holds row 8 (e / 4) + 4 (l / 32) + e % 4.
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][2], uint8_t *region, uint16_t *out, int M,
+                                           int ncols, int m0, int c0, int wave, int lane) {
+  const int wm = wave >> 2, wnn = wave & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int cc = 32 * j + (lane & 31);
+        *reinterpret_cast<uint16_t *>(region + rr * 128 + 16 * ((cc >> 3) ^ (rr & 7)) + 2 * (cc & 7)) =
+            f32_to_bf16(acc[i][j][e]);
+      }
+  __builtin_amdgcn_s_waitcnt(wait_imm(63, 0));
+#pragma unroll 4
+  for (int t = 0; t < 16; ++t) {
+    const int idx = t * 64 + lane;
+    const int rr = idx >> 3, c = idx & 7;
+    const uint4 v = *reinterpret_cast<const uint4 *>(region + rr * 128 + 16 * (c ^ (rr & 7)));
+    const int gr = m0 + 128 * wm + rr, gc = c0 + 64 * wnn + 8 * c;
+    if (gr < M && gc < ncols) *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(gr) * ncols + gc) = v;
+  }
+}
+
 // Workgroup -> (member, tile_row, tile_col).  Hardware spreads consecutive
 // workgroups over the 8 XCDs; remap so consecutive logical tiles (which share
 // rows of the left operand) run on the same XCD.  Member j of a grouped launch
@@ -397,18 +465,8 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const MatmulArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // LoRA steps: left = Ln [M, r] (T or G), right = B [N, r] or A [r, K].
   auto lora_steps = [&]() __attribute__((always_inline)) {
-    for (int j0 = 0; j0 < r; j0 += kBK) {
-      load_narrow(sX0, Ln, r, m0, M, j0);
-      if (kDx)
-        load_a_tile(sW0, Rn, r, K, j0, c0);
-      else
-        load_narrow(sW0, Rn, r, c0, N, j0);
-      __syncthreads();
-      mfma_stage<kDx>(sX0, sW0, ops, acc);
-      __syncthreads();
-    }
+    lora_tile_steps<kDx>(sX0, sW0, Ln, Rn, r, M, N, K, m0, c0, ops, acc);
   };
   if constexpr (kDrop) {
     lora_steps();
@@ -522,32 +580,111 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul(const MatmulArgs args) {
 
   if constexpr (!kDrop) lora_steps();
 
-  // Epilogue: the wave's 128 x 64 block as bf16 into its own 16 KB region
-  // (16-byte chunks XOR-swizzled by row), then 16-byte stores guarded by the
-  // matrix bounds (ncols % 8 == 0).  MFMA 32x32 output layout: lane l holds
-  // column l % 32; element e holds row 8 (e / 4) + 4 (l / 32) + e % 4.
   uint8_t *region = (wave < 2 ? sX0 : wave < 4 ? sX1 : wave < 6 ? sW0 : sW1) + (wave & 1) * 16384;
-  const int wm = wave >> 2, wnn = wave & 3;
+  store_tile(acc, region, out, M, ncols, m0, c0, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// The same products with the weight already dequantized: wd is the bf16
+// [N, K] matrix that the codec's dequantizer writes, bit for bit the values
+// the fused kernel expands, so the outputs are identical to k_matmul's.  The
+// weight tile is DMA'd like the left operand (the forward tile [256 n][64 k]
+// in the left operand's layout, the dX tile [64 n][256 k] in the layout the
+// transposed operand reads expect) one step ahead, and every wave only
+// multiplies: no table reads, scaling or expansion writes in the loop.  The
+// dX contraction (over N) has no zero-padded tail here: N % 64 == 0.
+template <bool kDx>
+__global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args) {
+  __shared__ __attribute__((aligned(16))) uint8_t sX0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sX1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sW0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sW1[kStageBytes];
+
+  int tr, tc;
+  const int mem = tile_coords(args, tr, tc);
+  const uint16_t *__restrict__ L = args.L[mem];
+  const uint16_t *__restrict__ Ln = args.Ln[mem];
+  const uint16_t *__restrict__ Rn = args.Rn[mem];
+  uint16_t *__restrict__ out = args.out[mem];
+  const uint16_t *__restrict__ Wd = args.wd[mem];
+  const int M = args.M[mem], r = args.r[mem];
+  const int K = args.w[mem].K, N = args.w[mem].N;
+  const int ncols = kDx ? K : N;
+  const int Kc = kDx ? N : K;
+  const int m0 = tr * kBM, c0 = tc * kBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KT = Kc / kBK;
+  auto dma_w = [&](uint8_t *ws, int kt) __attribute__((always_inline)) {
+    if (kDx)
+      dma_wdx(ws, Wd, N, K, kBK * kt, c0, wave, lane);
+    else
+      dma_left(ws, Wd, K, c0, N, kBK * kt, K, wave, lane);
+  };
+
+  const OpOffsets ops = op_offsets<kDx>();
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rr = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int cc = 32 * j + (lane & 31);
-        *reinterpret_cast<uint16_t *>(region + rr * 128 + 16 * ((cc >> 3) ^ (rr & 7)) + 2 * (cc & 7)) =
-            f32_to_bf16(acc[i][j][e]);
-      }
-  __builtin_amdgcn_s_waitcnt(wait_imm(63, 0));
-#pragma unroll 4
-  for (int t = 0; t < 16; ++t) {
-    const int idx = t * 64 + lane;
-    const int rr = idx >> 3, c = idx & 7;
-    const uint4 v = *reinterpret_cast<const uint4 *>(region + rr * 128 + 16 * (c ^ (rr & 7)));
-    const int gr = m0 + 128 * wm + rr, gc = c0 + 64 * wnn + 8 * c;
-    if (gr < M && gc < ncols) *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(gr) * ncols + gc) = v;
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  dma_left(sX0, L, Kc, m0, M, 0, Kc, wave, lane);
+  dma_w(sW0, 0);
+  raw_barrier<wait_imm(0, 0)>();
+
+  // Step kt multiplies stage CUR while both tiles of kt + 1 are DMA'd into
+  // the other stages; the end-of-step barrier waits for them.  As in the
+  // fused kernel, the operands of sub-step s + 1 are read while sub-step s
+  // multiplies and the last four MFMAs of a step run after its barrier.
+  Frag fa, fb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fb.a[i] = bf16x8_t{};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb.b[j] = bf16x8_t{};
+  auto step = [&](auto cur_tag, int kt) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    const uint8_t *xs = CUR ? sX1 : sX0;
+    const uint8_t *wr = CUR ? sW1 : sW0;
+    uint8_t *xn = CUR ? sX0 : sX1;
+    uint8_t *wn = CUR ? sW0 : sW1;
+    load_frag<kDx>(fa, xs, wr, ops, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows<2, 3>(fb, acc);
+    dma_left(xn, L, Kc, m0, M, min(kt + 1, KT - 1) * kBK, Kc, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows<3, 4>(fb, acc);
+    dma_w(wn, min(kt + 1, KT - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      Frag &cur = (s & 1) ? fb : fa;
+      Frag &nxt = (s & 1) ? fa : fb;
+      mfma_rows<0, 1>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 3) load_frag<kDx>(nxt, xs, wr, ops, s + 1);
+      mfma_rows<1, 2>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 3) mfma_rows<2, 4>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    raw_barrier<wait_imm(0, 0)>();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(C0(), kt);
+    step(C1(), kt + 1);
   }
+  if (kt < KT) step(C0(), kt);
+  mfma_rows<2, 4>(fb, acc);   // held back by the last step
+
+  lora_tile_steps<kDx>(sX0, sW0, Ln, Rn, r, M, N, K, m0, c0, ops, acc);
+  uint8_t *region = (wave < 2 ? sX0 : wave < 4 ? sX1 : wave < 6 ? sW0 : sW1) + (wave & 1) * 16384;
+  store_tile(acc, region, out, M, ncols, m0, c0, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,6 +719,40 @@ static hipError_t launch_mm_group(int count, const MatmulJob *jobs, hipStream_t 
 hipError_t launch_matmul_fwd_group(int count, const MatmulJob *jobs, hipStream_t s) {
   return launch_mm_group<false, false>(count, jobs, s);
 }
+
+// Products with dequantized weights (MatmulJob::wd set, w.N / w.K the shape).
+template <bool kDx>
+static hipError_t launch_pre_group(int count, const MatmulJob *jobs, hipStream_t s) {
+  if (count < 1 || count > kMmGroupMax) return hipErrorInvalidValue;
+  MatmulArgs a{};
+  a.n = count;
+  int tiles = 0;
+  for (int j = 0; j < count; ++j) {
+    const MatmulJob &jb = jobs[j];
+    const int ncols = kDx ? jb.w.K : jb.w.N;
+    a.L[j] = jb.L;
+    a.Ln[j] = jb.Ln;
+    a.Rn[j] = jb.Rn;
+    a.out[j] = jb.out;
+    a.w[j] = jb.w;
+    a.wd[j] = jb.wd;
+    a.M[j] = jb.M;
+    a.r[j] = jb.r;
+    a.tcols[j] = (ncols + kBN - 1) / kBN;
+    a.t0[j] = tiles;
+    tiles += ((jb.M + kBM - 1) / kBM) * a.tcols[j];
+  }
+  a.t0[count] = tiles;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_matmul_pre<kDx>), dim3(tiles), dim3(kThreadsMM), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pre_matmul_fwd_group(int count, const MatmulJob *jobs, hipStream_t s) {
+  return launch_pre_group<false>(count, jobs, s);
+}
+
+hipError_t launch_pre_matmul_dx(const MatmulJob &job, hipStream_t s) { return launch_pre_group<true>(1, &job, s); }
 
 hipError_t launch_matmul_fwd(const uint16_t *X, int M, const NF4View &w, const uint16_t *T,
                              const uint16_t *B, int r, uint16_t *Y, hipStream_t s) {

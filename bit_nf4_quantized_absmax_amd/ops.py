@@ -16,7 +16,7 @@ from dataclasses import dataclass
 
 import torch
 
-from ._capi import LoraGradsDescStruct, MatmulFwdDescStruct, NF4WeightStruct, check, lib
+from ._capi import DeqMatmulFwdDescStruct, LoraGradsDescStruct, MatmulFwdDescStruct, NF4WeightStruct, check, lib
 
 
 def _stream(t):
@@ -173,12 +173,20 @@ def quantize_group(Ws, qtypes=None):
     return outs
 
 
-def dequantize_group(weights):
-    """bf16 copies of up to 8 NF4Weights in one launch (qlora_dequantize_nf4_group)."""
+def dequantize_group(weights, outs=None):
+    """bf16 copies of up to 8 NF4Weights in one launch (qlora_dequantize_nf4_group),
+    into `outs` (bf16 [rows, cols] each) when given."""
     weights = list(weights)
     if not 1 <= len(weights) <= 8:
         raise ValueError("a group holds 1 to 8 weights")
-    outs = [torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device) for w in weights]
+    if outs is None:
+        outs = [torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device=w.device) for w in weights]
+    else:
+        outs = list(outs)
+        if len(outs) != len(weights):
+            raise ValueError("one output per weight")
+        for i, (w, o) in enumerate(zip(weights, outs)):
+            _need(o, torch.bfloat16, "outs[%d]" % i, (w.rows, w.cols))
     sts = (NF4WeightStruct * len(weights))(*[w.struct() for w in weights])
     ptrs = (ctypes.c_void_p * len(weights))(*[_ptr(o) for o in outs])
     check(lib().qlora_dequantize_nf4_group(len(weights), sts, ptrs, _stream(outs[0])), "qlora_dequantize_nf4_group")
@@ -477,6 +485,60 @@ def nf4_matmul_dx(dY, w, G, A, out=None):
     st = w.struct()
     check(lib().qlora_nf4_matmul_dx(_ptr(dY), M, ctypes.byref(st), _ptr(G), _ptr(A), r, _ptr(dX), _stream(dY)),
           "qlora_nf4_matmul_dx")
+    return dX
+
+
+def deq_matmul_fwd_group(members):
+    """Y_i = X_i Wd_i^T + T_i B_i^T from dequantized bf16 weights Wd_i [N, K]
+    (as dequantize / dequantize_group write them), up to 4 products sharing M
+    in one launch (qlora_deq_matmul_fwd_group).  members: sequence of dicts
+    with X, Wd, T, B and optional out.  Returns [Y, ...], bit-identical to
+    nf4_matmul_fwd on the weights the Wd were dequantized from."""
+    members = list(members)
+    if not 1 <= len(members) <= 4:
+        raise ValueError("a group holds 1 to 4 products")
+    descs, outs = [], []
+    for i, mb in enumerate(members):
+        X, Wd, T, B = mb["X"], mb["Wd"], mb["T"], mb["B"]
+        M = _mat(X, "members[%d].X" % i)[0]
+        N, K = _mat(Wd, "members[%d].Wd" % i)
+        r = _mat(B, "members[%d].B" % i)[1]
+        _need(X, torch.bfloat16, "members[%d].X" % i, (M, K))
+        _need(T, torch.bfloat16, "members[%d].T" % i, (M, r))
+        _need(B, torch.bfloat16, "members[%d].B" % i, (N, r))
+        Y = _out(mb.get("out"), (M, N), X.device, "members[%d].out" % i)
+        outs.append(Y)
+        descs.append(DeqMatmulFwdDescStruct(_ptr(X), M, _ptr(Wd), N, K, _ptr(T), _ptr(B), r, _ptr(Y)))
+    arr = (DeqMatmulFwdDescStruct * len(descs))(*descs)
+    check(lib().qlora_deq_matmul_fwd_group(len(descs), arr, _stream(members[0]["X"])), "qlora_deq_matmul_fwd_group")
+    return outs
+
+
+def deq_matmul_fwd(X, Wd, T, B, out=None):
+    """Y = X Wd^T + T B^T with Wd the dequantized bf16 weight [N, K]."""
+    M = _mat(X, "X")[0]
+    N, K = _mat(Wd, "Wd")
+    r = _mat(B, "B")[1]
+    _need(X, torch.bfloat16, "X", (M, K))
+    _need(T, torch.bfloat16, "T", (M, r))
+    _need(B, torch.bfloat16, "B", (N, r))
+    Y = _out(out, (M, N), X.device, "Y")
+    check(lib().qlora_deq_matmul_fwd(_ptr(X), M, _ptr(Wd), N, K, _ptr(T), _ptr(B), r, _ptr(Y), _stream(X)),
+          "qlora_deq_matmul_fwd")
+    return Y
+
+
+def deq_matmul_dx(dY, Wd, G, A, out=None):
+    """dX = dY Wd + G A with Wd the dequantized bf16 weight [N, K]."""
+    M = _mat(dY, "dY")[0]
+    N, K = _mat(Wd, "Wd")
+    r = _mat(A, "A")[0]
+    _need(dY, torch.bfloat16, "dY", (M, N))
+    _need(G, torch.bfloat16, "G", (M, r))
+    _need(A, torch.bfloat16, "A", (r, K))
+    dX = _out(out, (M, K), dY.device, "dX")
+    check(lib().qlora_deq_matmul_dx(_ptr(dY), M, _ptr(Wd), N, K, _ptr(G), _ptr(A), r, _ptr(dX), _stream(dY)),
+          "qlora_deq_matmul_dx")
     return dX
 
 

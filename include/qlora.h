@@ -363,6 +363,49 @@ int qlora_nf4_matmul_dx(const uint16_t *dY, int64_t M, const qlora_nf4_weight *W
                         const uint16_t *G, const uint16_t *A, int32_t r, uint16_t *dX,
                         void *stream);
 
+/* ---- The matmuls from a dequantized weight --------------------------------
+ * The same products as qlora_nf4_matmul_fwd / _fwd_group / _dx, with the
+ * weight given as its dequantized bf16 copy Wd [N, K] (row-major, 16-byte
+ * aligned), i.e. what qlora_dequantize_nf4 (or _group) writes for it.  The
+ * pages' recipe dequantizes the 4-bit weight to BFloat16 and then runs the
+ * matmul (automatone.win, "QLoRA paper explained", How it works; gptget.net,
+ * "QLoRA: Efficient Finetuning of Quantized LLMs", Deep Analysis /
+ * Methodology: 16-bit matmuls in both passes).  With Wd from the dequantizer
+ * the outputs are bit-identical to the fused entry points': the weight
+ * values and the contraction order are the same.  A training step can
+ * dequantize a layer's weights once (one grouped call) and use the copies
+ * for both the forward and the dX products; on gfx950 that is faster than
+ * expanding the codes inside every matmul tile (the caller holds N K 2 bytes
+ * per weight meanwhile).  No workspace; no decode-regime route (any M >= 0
+ * runs the 256 x 256 tiles).  Shape rules: K % 64 == 0, 1 <= r <= 128,
+ * N % 8 == 0 for the forward and N % 64 == 0 for dX.  M = 0 launches
+ * nothing. */
+int qlora_deq_matmul_fwd(const uint16_t *X, int64_t M, const uint16_t *Wd, int64_t N, int64_t K,
+                         const uint16_t *T, const uint16_t *B, int32_t r, uint16_t *Y, void *stream);
+
+/* One product of qlora_deq_matmul_fwd_group: the arguments of
+ * qlora_deq_matmul_fwd. */
+typedef struct {
+  const uint16_t *X;
+  int64_t M;
+  const uint16_t *Wd;
+  int64_t N;
+  int64_t K;
+  const uint16_t *T;
+  const uint16_t *B;
+  int32_t r;
+  uint16_t *Y;
+} qlora_deq_matmul_fwd_desc;
+
+/* Up to 4 such forward products sharing M in one launch over their
+ * concatenated tile grids (as qlora_nf4_matmul_fwd_group); each Y equals
+ * qlora_deq_matmul_fwd's.  Every member is validated before any launch;
+ * count outside 1..4, a NULL d or unequal M is INVALID_ARG. */
+int qlora_deq_matmul_fwd_group(int count, const qlora_deq_matmul_fwd_desc *d, void *stream);
+
+int qlora_deq_matmul_dx(const uint16_t *dY, int64_t M, const uint16_t *Wd, int64_t N, int64_t K,
+                        const uint16_t *G, const uint16_t *A, int32_t r, uint16_t *dX, void *stream);
+
 /* Workspace bytes for qlora_lora_grads (at least 256; 0 if unsupported). */
 size_t qlora_lora_grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 

@@ -274,6 +274,36 @@ def test_matmul_fwd_group_validation():
     assert L.qlora_nf4_matmul_fwd_group(2, zero, None) == OK             # M = 0: nothing launched
 
 
+def test_deq_matmul_validation():
+    L = q.lib()
+    P = 0x20000
+    # forward: (X, M, Wd, N, K, T, B, r, Y, stream)
+    assert L.qlora_deq_matmul_fwd(P, 8192, None, 4096, 4096, P, P, 64, P, None) == INVALID    # no weight
+    assert L.qlora_deq_matmul_fwd(P, 8192, 0x20008, 4096, 4096, P, P, 64, P, None) == INVALID  # misaligned weight
+    assert L.qlora_deq_matmul_fwd(P, 8192, P, 4096, 4000, P, P, 64, P, None) == SHAPE         # K % 64
+    assert L.qlora_deq_matmul_fwd(P, 8192, P, 4092, 4096, P, P, 64, P, None) == SHAPE         # N % 8
+    assert L.qlora_deq_matmul_fwd(P, 8192, P, 4096, 4096, P, P, 0, P, None) == SHAPE          # r
+    assert L.qlora_deq_matmul_fwd(P, -1, P, 4096, 4096, P, P, 64, P, None) == INVALID
+    assert L.qlora_deq_matmul_fwd(None, 8192, P, 4096, 4096, P, P, 64, P, None) == INVALID    # no X
+    assert L.qlora_deq_matmul_fwd(None, 0, P, 4096, 4096, None, P, 64, None, None) == OK      # M = 0
+    # dX: (dY, M, Wd, N, K, G, A, r, dX, stream); N % 64 on this route
+    assert L.qlora_deq_matmul_dx(P, 8192, P, 4104, 4096, P, P, 64, P, None) == SHAPE
+    assert L.qlora_deq_matmul_dx(P, 8192, P, 4096, 4096, P, None, 64, P, None) == INVALID     # no A
+    assert L.qlora_deq_matmul_dx(None, 0, P, 4096, 4096, None, P, 64, None, None) == OK
+    # group
+    Dm = _capi.DeqMatmulFwdDescStruct
+    ds = (Dm * 2)(Dm(P, 8192, P, 11008, 4096, P, P, 64, P), Dm(P, 8192, P, 11008, 4096, P, P, 64, P))
+    assert L.qlora_deq_matmul_fwd_group(0, ds, None) == INVALID
+    assert L.qlora_deq_matmul_fwd_group(5, ds, None) == INVALID
+    assert L.qlora_deq_matmul_fwd_group(2, None, None) == INVALID
+    uneq = (Dm * 2)(Dm(P, 8192, P, 11008, 4096, P, P, 64, P), Dm(P, 4096, P, 11008, 4096, P, P, 64, P))
+    assert L.qlora_deq_matmul_fwd_group(2, uneq, None) == INVALID
+    badk = (Dm * 2)(Dm(P, 8192, P, 11008, 4096, P, P, 64, P), Dm(P, 8192, P, 64, 100, P, P, 64, P))
+    assert L.qlora_deq_matmul_fwd_group(2, badk, None) == SHAPE
+    zero = (Dm * 1)(Dm(None, 0, P, 4096, 4096, None, P, 64, None))
+    assert L.qlora_deq_matmul_fwd_group(1, zero, None) == OK
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     W = torch.zeros(64, 64)
