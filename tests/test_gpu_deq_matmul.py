@@ -141,3 +141,24 @@ def test_deq_matmul_dx_rejects_n_not_multiple_of_64():
     Yf = q.nf4_matmul_fwd(d["X"], d["w"], d["T"], d["B"])
     torch.cuda.synchronize()
     _same(Y, Yf, "Y (N = 72)")
+
+
+@pytest.mark.parametrize("cfg_index,names", [(3, ("gate_proj", "down_proj")), (4, ("up_proj", "down_proj"))])
+def test_deq_matmul_larger_layers_bit_identical(cfg_index, names):
+    # the 33B (M = 8192) and 65B (M = 16384) shapes that the bench's layer
+    # figures run through this path: forward and dX, as the fused kernels
+    cfg = workloads.CONFIGS[cfg_index]
+    for i, lin in enumerate(l for l in cfg.linears if l.name in names):
+        print("deq matmul case", cfg.name, lin.name, cfg.tokens, flush=True)
+        d = _dev(cfg.tokens, lin.out_features, lin.in_features, cfg.rank, "nf4", 80 + 10 * cfg_index + i)
+        Y = q.deq_matmul_fwd(d["X"], d["Wd"], d["T"], d["B"])
+        Yf = q.nf4_matmul_fwd(d["X"], d["w"], d["T"], d["B"])
+        torch.cuda.synchronize()
+        _same(Y, Yf, "Y " + lin.name)
+        del Y, Yf
+        dX = q.deq_matmul_dx(d["dY"], d["Wd"], d["G"], d["A"])
+        dXf = q.nf4_matmul_dx(d["dY"], d["w"], d["G"], d["A"])
+        torch.cuda.synchronize()
+        _same(dX, dXf, "dX " + lin.name)
+        del d, dX, dXf
+        torch.cuda.empty_cache()
