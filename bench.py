@@ -81,6 +81,9 @@ def parse():
     p.add_argument("--matmul", choices=("deq", "fused"), default="deq",
                    help="deq: one grouped dequantize per step, then the matmuls from the bf16 weights; "
                         "fused: the NF4 codes expanded inside every matmul tile")
+    p.add_argument("--vendor-gemm-only", action="store_true",
+                   help="only a same-process comparison of the matmul launches with the vendor library's "
+                        "plain bf16 GEMM (torch.mm) on the 7B shapes, as one JSON line")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB first (a reference "
                         "dispatch for scaling hardware byte counters)")
@@ -177,6 +180,65 @@ def _timed(events, key, torch, grp):
                                        grp))
     events[key][-1][0].record()
     return events[key][-1][1]
+
+
+def vendor_gemm_bench(q, torch, workloads, cfg, dev, reps=10, rounds=3):
+    """The dequantized-weight matmuls against the vendor library's plain bf16
+    GEMM (torch.mm, which dispatches to hipBLASLt) on the same operands, one
+    process, alternating (the library's forward allocates its output per
+    call, through torch's caching allocator): a reference for what a tuned
+    library reaches on
+    these shapes on this chip.  Both are timed on the base product's 2 M N K
+    FLOP; ours also runs the rank-r LoRA contraction steps (Y += T B^T,
+    dX += G A) inside the same launch, which the library call does not."""
+    M, r = cfg.tokens, cfg.rank
+    bf = torch.bfloat16
+    out = {}
+    shapes = []
+    for lin in cfg.linears:
+        key = (lin.out_features, lin.in_features)
+        if key not in shapes:
+            shapes.append(key)
+    for si, (N, K) in enumerate(shapes):
+        seed = 77000 + 10 * si
+        X = workloads.device_normal((M, K), 1.0, seed, dev, bf)
+        Wd = workloads.device_normal((N, K), workloads.W_STD, seed + 1, dev, bf)
+        dY = workloads.device_normal((M, N), 1.0, seed + 2, dev, bf)
+        T = workloads.device_normal((M, r), 1.0, seed + 3, dev, bf)
+        G = workloads.device_normal((M, r), 1.0, seed + 4, dev, bf)
+        A = workloads.device_normal((r, K), workloads.LORA_STD, seed + 5, dev, bf)
+        B = workloads.device_normal((N, r), workloads.LORA_STD, seed + 6, dev, bf)
+        Y = torch.empty(M, N, dtype=bf, device=dev)
+        dX, dXv = torch.empty(M, K, dtype=bf, device=dev), torch.empty(M, K, dtype=bf, device=dev)
+        calls = {
+            "fwd_ours": lambda: q.deq_matmul_fwd(X, Wd, T, B, out=Y),
+            "fwd_vendor": lambda: torch.nn.functional.linear(X, Wd),
+            "dx_ours": lambda: q.deq_matmul_dx(dY, Wd, G, A, out=dX),
+            "dx_vendor": lambda: torch.mm(dY, Wd, out=dXv),
+        }
+        times = {k: [] for k in calls}
+        for fn in calls.values():
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(rounds):
+            for k, fn in calls.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times[k].append(e0.elapsed_time(e1) * 1e3 / reps)
+        flops = 2.0 * M * N * K
+        ent = dict(M=M, N=N, K=K, r=r)
+        for k, ts in times.items():
+            us = min(ts)
+            ent[k] = dict(us=round(us, 1), TFLOPs=round(flops / (us * 1e-6) / 1e12, 1),
+                          frac_bf16_peak=round(flops / (us * 1e-6) / 2.5e15, 4))
+        out["N%d_K%d" % (N, K)] = ent
+        del X, Wd, dY, T, G, A, B, Y, dX, dXv
+        torch.cuda.empty_cache()
+    return out
 
 
 def run_step(q, torch, layers, scale, events=None, mode="deq"):
@@ -782,6 +844,13 @@ def main():
                            graphs=not args.small_m_eager, patterns=pats)
         print(json.dumps(dict(metric="small-M dequant forward GB/s (7B layer, 7 linears, 4 weight sets)",
                               unit="GB/s", data="synthetic", small_m=sm)), flush=True)
+        return
+    if args.vendor_gemm_only:
+        c1 = workloads.CONFIGS[1]
+        print(json.dumps(dict(metric="dequantized-weight matmul vs vendor bf16 GEMM (7B shapes, 8192 tokens)",
+                              unit="TFLOP/s", data="synthetic",
+                              note="min over 3 rounds of 10 launches each, alternating; FLOP = 2 M N K for both",
+                              vendor_gemm=vendor_gemm_bench(q, torch, workloads, c1, dev))), flush=True)
         return
     if args.codec_only:
         c1 = workloads.CONFIGS[1]
