@@ -190,7 +190,10 @@ def vendor_gemm_bench(q, torch, workloads, cfg, dev, reps=10, rounds=3):
     library reaches on
     these shapes on this chip.  Both are timed on the base product's 2 M N K
     FLOP; ours also runs the rank-r LoRA contraction steps (Y += T B^T,
-    dX += G A) inside the same launch, which the library call does not."""
+    dX += G A) inside the same launch, which the library call does not.
+    The LoRA products T = X A^T, G = dY B and dA = G^T X, dB = dY^T T are
+    compared the same way, as HBM rates on their algorithmic bytes (each
+    operand read once, each output written once)."""
     M, r = cfg.tokens, cfg.rank
     bf = torch.bfloat16
     out = {}
@@ -235,8 +238,44 @@ def vendor_gemm_bench(q, torch, workloads, cfg, dev, reps=10, rounds=3):
             us = min(ts)
             ent[k] = dict(us=round(us, 1), TFLOPs=round(flops / (us * 1e-6) / 1e12, 1),
                           frac_bf16_peak=round(flops / (us * 1e-6) / 2.5e15, 4))
+        # The LoRA products (HBM-bound): ours (T and G carry the scale; dA and dB
+        # in one call) against the library's plain products on the same operands.
+        Tv, Gv = torch.empty(M, r, dtype=bf, device=dev), torch.empty(M, r, dtype=bf, device=dev)
+        dA, dB = torch.empty(r, K, dtype=bf, device=dev), torch.empty(N, r, dtype=bf, device=dev)
+        dAv, dBv = torch.empty(r, K, dtype=bf, device=dev), torch.empty(N, r, dtype=bf, device=dev)
+        To, Go = torch.empty(M, r, dtype=bf, device=dev), torch.empty(M, r, dtype=bf, device=dev)
+        gws = torch.empty(max(q.lib().qlora_lora_grad_in_workspace_bytes(N, r), 16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(q.lib().qlora_lora_grads_workspace_bytes(M, N, K, r), 16), dtype=torch.uint8, device=dev)
+        At, Gt, dYt = A.t(), G.t(), dY.t()
+        lcalls = {
+            "T_ours": lambda: q.lora_down(X, A, cfg.scale, out=To),
+            "T_vendor": lambda: torch.mm(X, At, out=Tv),
+            "G_ours": lambda: q.lora_grad_in(dY, B, cfg.scale, out=Go, workspace=gws),
+            "G_vendor": lambda: torch.mm(dY, B, out=Gv),
+            "dAdB_ours": lambda: q.lora_grads(X, dY, G, T, workspace=ws, dA_out=dA, dB_out=dB),
+            "dAdB_vendor": lambda: (torch.mm(Gt, X, out=dAv), torch.mm(dYt, T, out=dBv)),
+        }
+        lbytes = {"T": 2.0 * (M * K + r * K + M * r), "G": 2.0 * (M * N + N * r + M * r),
+                  "dAdB": 2.0 * (M * K + M * N + 2 * M * r + r * K + N * r)}
+        ltimes = {k: [] for k in lcalls}
+        for fn in lcalls.values():
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(rounds):
+            for k, fn in lcalls.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ltimes[k].append(e0.elapsed_time(e1) * 1e3 / reps)
+        for k, ts in ltimes.items():
+            us = min(ts)
+            nb = lbytes[k.split("_")[0]]
+            ent[k] = dict(us=round(us, 1), GBps=round(nb / (us * 1e-6) / 1e9, 1), frac_hbm=round(nb / (us * 1e-6) / 8e12, 4))
         out["N%d_K%d" % (N, K)] = ent
-        del X, Wd, dY, T, G, A, B, Y, dX, dXv
+        del X, Wd, dY, T, G, A, B, Y, dX, dXv, Tv, Gv, dA, dB, dAv, dBv, To, Go, gws, ws, At, Gt, dYt
         torch.cuda.empty_cache()
     return out
 
