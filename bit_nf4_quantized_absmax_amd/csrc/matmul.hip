@@ -615,7 +615,7 @@ constexpr int kPreBand = 4;
 // transposed operand reads expect) one step ahead, and every wave only
 // multiplies: no table reads, scaling or expansion writes in the loop.  The
 // dX contraction (over N) has no zero-padded tail here: N % 64 == 0.
-template <bool kDx>
+template <bool kDx, bool kPipe>
 __global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t sX0[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sX1[kStageBytes];
@@ -637,11 +637,27 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KT = Kc / kBK;
+  // kPipe (every member has r == 64 and an even step count): the LoRA step
+  // is one more step of the same pipeline.  T or G [M, 64] and B [N, 64]
+  // have the left operand's 128-byte row layout and A [64, K] the dX weight
+  // tile's, so the last contraction step DMAs them like the next tile (no
+  // zero padding: j < r throughout).  Otherwise the LoRA tiles are staged
+  // after the loop.
+  auto dma_x = [&](uint8_t *xs, int kt) __attribute__((always_inline)) {
+    dma_left(xs, L, Kc, m0, M, kBK * kt, Kc, wave, lane);
+  };
   auto dma_w = [&](uint8_t *ws, int kt) __attribute__((always_inline)) {
     if (kDx)
       dma_wdx(ws, Wd, N, K, kBK * kt, c0, wave, lane);
     else
       dma_left(ws, Wd, K, c0, N, kBK * kt, K, wave, lane);
+  };
+  auto dma_lora = [&](uint8_t *xs, uint8_t *ws) __attribute__((always_inline)) {
+    dma_left(xs, Ln, r, m0, M, 0, r, wave, lane);
+    if (kDx)
+      dma_wdx(ws, Rn, r, K, 0, c0, wave, lane);
+    else
+      dma_left(ws, Rn, r, c0, N, 0, r, wave, lane);
   };
 
   const OpOffsets ops = op_offsets<kDx>();
@@ -653,7 +669,7 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  dma_left(sX0, L, Kc, m0, M, 0, Kc, wave, lane);
+  dma_x(sX0, 0);
   dma_w(sW0, 0);
   raw_barrier<wait_imm(0, 0)>();
 
@@ -666,8 +682,11 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args
   for (int i = 0; i < 4; ++i) fb.a[i] = bf16x8_t{};
 #pragma unroll
   for (int j = 0; j < 2; ++j) fb.b[j] = bf16x8_t{};
-  auto step = [&](auto cur_tag, int kt) __attribute__((always_inline)) {
+  // kMode 0: DMA step kt + 1 (clamped to the last step); 1: DMA the LoRA
+  // tiles (the last contraction step of kPipe); 2: no DMA.
+  auto step = [&](auto cur_tag, auto mode_tag, int kt) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_tag)::value;
+    constexpr int kMode = decltype(mode_tag)::value;
     const uint8_t *xs = CUR ? sX1 : sX0;
     const uint8_t *wr = CUR ? sW1 : sW0;
     uint8_t *xn = CUR ? sX0 : sX1;
@@ -675,10 +694,11 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args
     load_frag<kDx>(fa, xs, wr, ops, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_rows<2, 3>(fb, acc);
-    dma_left(xn, L, Kc, m0, M, min(kt + 1, KT - 1) * kBK, Kc, wave, lane);
+    if (kMode == 0) dma_x(xn, min(kt + 1, KT - 1));
+    if (kMode == 1) dma_lora(xn, wn);
     __builtin_amdgcn_sched_barrier(0);
     mfma_rows<3, 4>(fb, acc);
-    dma_w(wn, min(kt + 1, KT - 1));
+    if (kMode == 0) dma_w(wn, min(kt + 1, KT - 1));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -696,15 +716,26 @@ __global__ __launch_bounds__(kThreadsMM) void k_matmul_pre(const MatmulArgs args
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
   int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(C0(), kt);
-    step(C1(), kt + 1);
+  if constexpr (kPipe) {
+    for (; kt + 2 < KT; kt += 2) {
+      step(C0(), C0(), kt);
+      step(C1(), C0(), kt + 1);
+    }
+    step(C0(), C0(), KT - 2);
+    step(C1(), C1(), KT - 1);
+    step(C0(), C2(), KT);
+    mfma_rows<2, 4>(fb, acc);   // held back by the last step
+  } else {
+    for (; kt + 2 <= KT; kt += 2) {
+      step(C0(), C0(), kt);
+      step(C1(), C0(), kt + 1);
+    }
+    if (kt < KT) step(C0(), C0(), kt);
+    mfma_rows<2, 4>(fb, acc);   // held back by the last step
+    lora_tile_steps<kDx>(sX0, sW0, Ln, Rn, r, M, N, K, m0, c0, ops, acc);
   }
-  if (kt < KT) step(C0(), kt);
-  mfma_rows<2, 4>(fb, acc);   // held back by the last step
-
-  lora_tile_steps<kDx>(sX0, sW0, Ln, Rn, r, M, N, K, m0, c0, ops, acc);
   uint8_t *region = (wave < 2 ? sX0 : wave < 4 ? sX1 : wave < 6 ? sW0 : sW1) + (wave & 1) * 16384;
   store_tile(acc, region, out, M, ncols, m0, c0, wave, lane);
 }
@@ -766,7 +797,12 @@ static hipError_t launch_pre_group(int count, const MatmulJob *jobs, hipStream_t
   }
   a.t0[count] = tiles;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_matmul_pre<kDx>), dim3(tiles), dim3(kThreadsMM), 0, s, a);
+  bool pipe = true;
+  for (int j = 0; j < count; ++j) pipe = pipe && jobs[j].r == kBK && ((kDx ? jobs[j].w.N : jobs[j].w.K) / kBK) % 2 == 0;
+  if (pipe)
+    hipLaunchKernelGGL((k_matmul_pre<kDx, true>), dim3(tiles), dim3(kThreadsMM), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_matmul_pre<kDx, false>), dim3(tiles), dim3(kThreadsMM), 0, s, a);
   return hipGetLastError();
 }
 

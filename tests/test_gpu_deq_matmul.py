@@ -37,9 +37,12 @@ def _same(a, b, name):
 
 # M >= 65 (the fused kernels' tile route): ragged row tiles, N and K that
 # leave partial column tiles, r not a multiple of 8 and r over 64 (two LoRA
-# steps), the three 4-bit tables.
+# steps), the three 4-bit tables.  r = 64 with an even number of 64-deep
+# contraction steps runs the LoRA step inside the DMA pipeline (two steps is
+# the shortest such loop); r = 64 with an odd count stages it after the loop.
 CASES = [(300, 1024, 512, 64, "nf4"), (257, 576, 1088, 12, "fp4"), (513, 1344, 704, 96, "int4"),
-         (65, 64, 64, 128, "nf4"), (1000, 2048, 4096, 8, "nf4")]
+         (65, 64, 64, 128, "nf4"), (1000, 2048, 4096, 8, "nf4"), (300, 704, 576, 64, "nf4"),
+         (130, 128, 128, 64, "fp4")]
 
 
 @pytest.mark.parametrize("M,N,K,r,qtype", CASES)
