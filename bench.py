@@ -444,9 +444,9 @@ def small_m_bench(q, torch, workloads, cfg, dev, reps=200, graphs=True, patterns
                              reps=reps, GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
             del graph
         if "per_linear" in res:
-            res["per_linear"]["launches_per_layer"] = (2 if M <= 16 else 4) * len(cfg.linears)
+            res["per_linear"]["launches_per_layer"] = (2 if M <= 16 else 3) * len(cfg.linears)
         if "grouped" in res:
-            res["grouped"]["launches_per_layer"] = 2 if M <= 4 else 4
+            res["grouped"]["launches_per_layer"] = 2 if M <= 4 else 3
         res["bytes_per_layer"] = int(nbytes)
         out["M%d" % M] = res
     del sets

@@ -124,6 +124,7 @@ struct SmLinear {
   const uint16_t *B;
   const uint16_t *Tin;
   float *P;
+  float *Pd;    // stream path: the down-projection partials [K / 256][M][r] fp32
   uint16_t *Y;
   uint16_t *Tout;
   int r;

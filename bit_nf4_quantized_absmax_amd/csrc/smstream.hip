@@ -4,12 +4,12 @@
 // (automatone.win, "QLoRA paper explained", How it works: the 4-bit weights
 // are dequantized on the fly for the math and never stored in 16-bit.)
 //
-// The work is bound by the packed-weight stream from HBM; four kernels:
+// The work is bound by the packed-weight stream from HBM; three kernels:
 //  * k_ss_down: partial down-projections X[:, c] A[:, c]^T per 256-column
 //    chunk c (fp32), one workgroup per (linear, chunk, 64 adapter rows);
-//  * k_ss_finish: T = bf16(s * sum of the partials in chunk order) (also to
-//    the caller's T_out);
-//  * k_ss_stream: one workgroup per CU, persistent.  Work unit = (linear, 64
+//  * k_ss_stream: one workgroup per CU, persistent.  It first forms its
+//    share of T = bf16(s * sum of the partials in chunk order) (also to the
+//    caller's T_out), beside its first weight DMAs.  Work unit = (linear, 64
 //    weight rows, 256 columns); units are ordered by linear, row tile and
 //    column and every workgroup takes an equal contiguous range, so each CU
 //    streams the same number of bytes.  A unit's packed bytes (64 rows x 128
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kSsDownThreads) void k_ss_down(SmGroup grp) {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[s][mb], av[s], acc[mb], 0, 0, 0);
   // D layout: lane holds column (adapter row) j, tokens 4 g + e.
-  float *P = L.P + static_cast<int64_t>(c) * M * r;
+  float *P = L.Pd + static_cast<int64_t>(c) * M * r;
   if (j < r) {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
@@ -141,30 +141,6 @@ __global__ __launch_bounds__(kSsDownThreads) void k_ss_down(SmGroup grp) {
         if (m < M) P[static_cast<int64_t>(m) * r + j] = acc[mb][e];
       }
   }
-}
-
-// T = bf16(s * sum over chunks of P) in chunk order, to the workspace copy
-// and T_out (blocks from main_start).
-__global__ __launch_bounds__(256) void k_ss_finish(SmGroup grp) {
-  int li = 0;
-  while (li + 1 < grp.n && static_cast<int>(blockIdx.x) >= grp.main_start[li + 1]) ++li;
-  const SmLinear &L = grp.lin[li];
-  const int M = grp.M, r = L.r;
-  const int i = (blockIdx.x - grp.main_start[li]) * 256 + threadIdx.x;
-  if (i >= M * r) return;
-  const int KT = L.w.K / kSsStepK;             // <= kSsMaxKT
-  const int64_t stride = static_cast<int64_t>(M) * r;
-  // Every chunk's load in flight at once, then the sum in chunk order.
-  float pv[kSsMaxKT];
-#pragma unroll
-  for (int c = 0; c < kSsMaxKT; ++c) pv[c] = c < KT ? L.P[c * stride + i] : 0.f;
-  float t = 0.f;
-#pragma unroll
-  for (int c = 0; c < kSsMaxKT; ++c)
-    if (c < KT) t += pv[c];
-  const uint16_t v = f32_to_bf16(L.scale * t);
-  const_cast<uint16_t *>(L.Tin)[i] = v;
-  if (L.Tout) L.Tout[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -452,6 +428,43 @@ __global__ __launch_bounds__(kSsThreads) void k_ss_stream(SmGroup grp) {
     issue_w();
     issue_w();
   }
+  // T for the epilogue kernel while those DMAs fly: this workgroup's equal
+  // share of the M r elements of every linear (main_start: prefix sums),
+  // each the sum of its chunk partials in chunk order.  The partial loads
+  // are younger than the DMAs, so their waits also cover the DMAs, which the
+  // first round needs anyway.
+  {
+    const int E = grp.main_start[grp.n];
+    const int e0 = static_cast<int>((static_cast<int64_t>(w) * E) / G);
+    const int e1 = static_cast<int>((static_cast<int64_t>(w + 1) * E) / G);
+    for (int li = 0; li < grp.n; ++li) {          // uniform: the share's part in each linear
+      const int lo = max(e0, grp.main_start[li]) - grp.main_start[li];
+      const int hi = min(e1, grp.main_start[li + 1]) - grp.main_start[li];
+      if (lo >= hi) continue;
+      const SmLinear &L = grp.lin[li];
+      const int KT = L.w.K / kSsStepK;             // <= kSsMaxKT
+      for (int i = lo + tid; i < hi; i += kSsThreads) {
+        // addresses formed in vector registers (the stream loop needs the
+        // scalar ones), 16 chunk loads in flight, summed in chunk order
+        int stride = M * L.r;
+        asm volatile("" : "+v"(stride));
+        const float *pp = L.Pd + i;
+        float t = 0.f;
+        for (int c0 = 0; c0 < KT; c0 += 16) {
+          float pv[16];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) pv[c] = c0 + c < KT ? pp[c * stride] : 0.f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c)
+            if (c0 + c < KT) t += pv[c];
+          pp += 16 * stride;
+        }
+        const uint16_t v = f32_to_bf16(L.scale * t);
+        const_cast<uint16_t *>(L.Tin)[i] = v;
+        if (L.Tout) L.Tout[i] = v;
+      }
+    }
+  }
   round_end();
 
   f32x4_t acc[kPT][2][kMB];
@@ -611,21 +624,22 @@ bool small_m_stream_ok(int64_t M, int K, int r) {
   return M > 4 && M <= 64 && r % 8 == 0 && K >= kSsStepK && K % kSsStepK == 0 && K / kSsStepK <= kSsMaxKT;
 }
 
-// Per linear: chunk partials [K / 256][M][r] fp32, the segment slots
-// ((groups + workgroups) x kPT pieces of 64 rows x 16 kMB tokens, fp32) and
-// T [M][r] bf16.  The chunk partials and the slots
-// share the first part: the slots are written by the stream kernel after
-// k_ss_finish has consumed the partials.
-static size_t ss_share_bytes(int M, int N, int K, int r) {
+// Per linear: the segment slots ((groups + workgroups) x kPT pieces of 64
+// rows x 16 kMB tokens, fp32), the down-projection partials [K / 256][M][r]
+// fp32 (read by the stream kernel while other workgroups already write
+// slots, hence their own region) and T [M][r] bf16.
+static size_t ss_slot_bytes(int M, int N, int K, int r) {
   const int kmb = (M + 15) / 16, pt = ss_pt_of(kmb);
-  const size_t p = static_cast<size_t>(K / kSsStepK) * M * r * 4;
   const int tiles = (N + kSsRows - 1) / kSsRows;
   const size_t groups = static_cast<size_t>((tiles + pt - 1) / pt);
   const size_t slots = (groups + kSsMaxGrid) * pt * (2 * 2 * kmb * 4 * 64) * 4;
-  return (std::max(p, slots) + 255) / 256 * 256;
+  return (slots + 255) / 256 * 256;
+}
+static size_t ss_part_bytes(int M, int K, int r) {
+  return (static_cast<size_t>(K / kSsStepK) * M * r * 4 + 255) / 256 * 256;
 }
 size_t small_m_stream_ws_bytes(int M, int N, int K, int r) {
-  return ss_share_bytes(M, N, K, r) + (static_cast<size_t>(M) * r * 2 + 255) / 256 * 256;
+  return ss_slot_bytes(M, N, K, r) + ss_part_bytes(M, K, r) + (static_cast<size_t>(M) * r * 2 + 255) / 256 * 256;
 }
 
 bool small_m_stream_group_ok(const SmGroup &grp) {
@@ -651,9 +665,6 @@ static hipError_t ss_launch(SmGroup &grp, hipStream_t s) {
   hipLaunchKernelGGL(k_ss_down<kMB>, dim3(grp.down_start[grp.n]), dim3(kSsDownThreads), 0, s, grp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_ss_finish, dim3(grp.main_start[grp.n]), dim3(256), 0, s, grp);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_ss_stream<kMB>, dim3(grid), dim3(kSsThreads), 0, s, grp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -663,20 +674,22 @@ static hipError_t ss_launch(SmGroup &grp, hipStream_t s) {
 
 // Each linear's L.P is the start of its workspace region
 // (small_m_stream_ws_bytes).  Plans tiles (item0), down-projection blocks
-// (down_start) and finish blocks (main_start); ss_launch plans the units.
+// (down_start) and each linear's first T element (main_start); ss_launch
+// plans the units.
 hipError_t launch_small_m_stream(SmGroup &grp, hipStream_t s) {
   int tiles = 0, down = 0, fin = 0;
   for (int i = 0; i < grp.n; ++i) {
     SmLinear &L = grp.lin[i];
     const int M = grp.M, N = L.w.N, K = L.w.K, r = L.r;
     char *base = reinterpret_cast<char *>(L.P);
-    L.Tin = reinterpret_cast<const uint16_t *>(base + ss_share_bytes(M, N, K, r));
+    L.Pd = reinterpret_cast<float *>(base + ss_slot_bytes(M, N, K, r));
+    L.Tin = reinterpret_cast<const uint16_t *>(base + ss_slot_bytes(M, N, K, r) + ss_part_bytes(M, K, r));
     grp.item0[i] = tiles;
     grp.down_start[i] = down;
     grp.main_start[i] = fin;
     tiles += (N + kSsRows - 1) / kSsRows;
     down += (K / kSsStepK) * ((r + 63) / 64);
-    fin += (M * r + 255) / 256;
+    fin += M * r;
   }
   grp.item0[grp.n] = tiles;
   grp.down_start[grp.n] = down;
