@@ -942,7 +942,7 @@ def main():
     dom = kern[dom_key]
     achieved = dom["flops_per_launch"] / (dom["avg_us"] * 1e-6) / 1e12
     if args.matmul == "deq":
-        dom_kernel = "qlora::k_matmul_pre<false>" if dom_key == "fwd" else "qlora::k_matmul_pre<true>"
+        dom_kernel = "qlora::k_matmul_pre<false, true>" if dom_key == "fwd" else "qlora::k_matmul_pre<true, true>"
     else:
         dom_kernel = "qlora::k_matmul<false, false>" if dom_key == "fwd" else "qlora::k_matmul<true, false>"
     roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
