@@ -19,7 +19,7 @@ QLORA_ERR_SCRATCH_LIMIT = -5
 STATIC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
-    "qlora_status_string", "qlora_version", "qlora_nf4_sizes",
+    "qlora_status_string", "qlora_version", "qlora_small_m_max", "qlora_nf4_sizes",
     "qlora_quantize_workspace_bytes", "qlora_quantize_nf4", "qlora_quantize_nf4_16", "qlora_dequantize_nf4",
     "qlora_quantize_group_workspace_bytes", "qlora_quantize_nf4_group", "qlora_dequantize_nf4_group",
     "qlora_linear_workspace_bytes", "qlora_linear_fwd", "qlora_linear_fwd_noalloc", "qlora_linear_bwd",
@@ -114,6 +114,7 @@ _wp = ctypes.POINTER(NF4WeightStruct)
 _SIGS = {
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_version": (ctypes.c_int, []),
+    "qlora_small_m_max": (ctypes.c_int, []),
     "qlora_nf4_sizes": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "qlora_quantize_workspace_bytes": (_sz, [_i64]),
     "qlora_quantize_nf4": (ctypes.c_int, [_vp, _wp, _vp, _sz, _vp]),

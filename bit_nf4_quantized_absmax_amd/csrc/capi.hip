@@ -151,6 +151,8 @@ const char *qlora_status_string(int status) {
 
 int qlora_version(void) { return 10000; }
 
+int qlora_small_m_max(void) { return small_m_max(); }
+
 int qlora_nf4_sizes(int64_t n, int64_t *packed_bytes, int64_t *nb, int64_t *nb2) {
   if (n < 1) return QLORA_ERR_INVALID_ARG;
   const int64_t b = (n + 63) / 64;

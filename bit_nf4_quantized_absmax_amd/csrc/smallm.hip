@@ -23,6 +23,7 @@
 //   T B^T, T = bf16(s * sum of the partials) (or T as given).  The 16 wave
 //   accumulators are summed in LDS in wave order: results are deterministic.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.h"
 #include "launch.h"
@@ -40,7 +41,21 @@ constexpr int kSmDownSteps = 8;       // 32-column MFMA steps per load batch in 
 constexpr int kSmMaxSplits = 2;       // column chunks of the down-projection (partials)
 constexpr int kSmWait0 = 0xC07F;      // s_waitcnt lgkmcnt(0)
 
-int small_m_max() { return kSmMaxM; }
+// The decode-regime threshold: kSmMaxM, or the environment variable
+// QLORA_SMALL_M_MAX (a decimal integer, clamped to [0, kSmMaxM]; read once per
+// process), so that the tile kernels can be timed at small M.  0 sends every
+// M to the tile kernels.
+int small_m_max() {
+  static const int v = [] {
+    const char *e = getenv("QLORA_SMALL_M_MAX");
+    if (!e || !*e) return kSmMaxM;
+    char *end = nullptr;
+    const long x = strtol(e, &end, 10);
+    if (!end || *end != '\0' || x < 0) return kSmMaxM;
+    return static_cast<int>(std::min<long>(x, kSmMaxM));
+  }();
+  return v;
+}
 
 __device__ __forceinline__ void sm_barrier_lds_only() {
   // Barrier after LDS writes that leaves this wave's global loads in flight
@@ -364,7 +379,7 @@ static int sm_splits(int M, int K, int *kw_out) {
   return (K + kSmWaves * kw - 1) / (kSmWaves * kw);
 }
 
-bool small_m_ok(int64_t M, int r) { return M >= 1 && M <= kSmMaxM && r % 8 == 0; }
+bool small_m_ok(int64_t M, int r) { return M >= 1 && M <= small_m_max() && r % 8 == 0; }
 
 size_t small_m_ws_bytes(int M, int K, int r) {
   int S = sm_splits(M, K, nullptr);

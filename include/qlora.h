@@ -111,6 +111,16 @@ const char *qlora_status_string(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int qlora_version(void);
 
+/* Largest M the forward sends to the decode-regime kernels (dequant-GEMV and
+ * weight stream: the small-M case of the pages' dequantize-then-multiply,
+ * automatone.win, "QLoRA paper explained", How it works); larger M take the
+ * tiled MFMA matmuls.  64 by default; the environment variable
+ * QLORA_SMALL_M_MAX (a decimal integer, clamped to [0, 64], read once per
+ * process) lowers it for benchmarking the tiled kernels at small M, 0 sending
+ * every M there.  Results stay within the matmul tolerance either way (the two
+ * routes round differently).  Host-only; never touches the GPU. */
+int qlora_small_m_max(void);
+
 /* Storage sizes for n >= 1 elements: packed bytes, blocks (nb), groups (nb2).
  * Any output pointer may be NULL.  Host-only; never touches the GPU. */
 int qlora_nf4_sizes(int64_t n, int64_t *packed_bytes, int64_t *nb, int64_t *nb2);

@@ -349,3 +349,27 @@ def test_noalloc_forward_validates_before_touching_the_gpu():
     assert L.qlora_linear_fwd_noalloc(None, 0, ctypes.byref(w), P, P, 8, 1.0, None, None, None) == OK
     assert "SCRATCH" in q.status_string(-5)
     assert _capi.STATIC_SCRATCH_BYTES == 16 << 20
+
+
+def _small_m_max_with(value):
+    # The threshold is read once per process, so each setting gets its own
+    # interpreter (host only: the query never touches the GPU).
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("QLORA_SMALL_M_MAX", None)
+    if value is not None:
+        env["QLORA_SMALL_M_MAX"] = value
+    code = ("import ctypes; L = ctypes.CDLL(%r); print(L.qlora_small_m_max())" % _capi.LIB_PATH)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    return int(out.stdout.strip().splitlines()[-1])
+
+
+def test_small_m_threshold_switch():
+    assert _small_m_max_with(None) == 64
+    assert _small_m_max_with("16") == 16
+    assert _small_m_max_with("0") == 0
+    assert _small_m_max_with("1000") == 64   # clamped to the decode kernels' limit
+    assert _small_m_max_with("-3") == 64     # not a count: the default
+    assert _small_m_max_with("12abc") == 64
